@@ -1,0 +1,36 @@
+"""Plain fp64 CPU oracle for single-token decode attention over a KV cache.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute anything in this package: only the test suite, the smoke check in
+``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` use it.
+It shares no code, constant or helper with the HIP library under
+``mla_kv_cache_amd/``; the two meet only through the seeded input
+generators in ``workloads/``, which hold none of the method's arithmetic.
+
+What it computes is the plain definition of the method, written out in
+float64 on the exact input values (bf16 inputs are widened exactly):
+
+* ``attention.decode_gqa`` -- one query token per head against a cache of
+  ``h_kv`` shared K/V heads; MHA when ``h_kv == h_q``, MQA when ``h_kv == 1``.
+* ``attention.decode_mla`` -- absorbed multi-head latent attention: every
+  head scores against one cached latent plus a decoupled rotary key, and
+  averages the latent itself.
+* ``cache.kv_cache_bytes`` / ``cache.mla_cache_bytes`` -- the cache-size
+  arithmetic.
+* ``brute`` -- pure-Python scalar loops for tiny shapes (a second,
+  structurally different statement of the same definition).
+
+Every function is pinned by tests that do not re-type its formula: the
+pages' printed numbers, closed forms, invariants, a library routine
+(PyTorch's scaled-dot-product attention on CPU in float64) and brute force.
+No function here is "parity unpinned".
+"""
+
+from .attention import (  # noqa: F401
+    decode_gqa,
+    decode_mla,
+    decode_gqa_weights,
+    clamp_len,
+)
+from .cache import kv_cache_bytes, mla_cache_bytes  # noqa: F401
+from . import brute  # noqa: F401

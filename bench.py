@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X: KV-cache GB/s per decode step.
+
+A step is one decode step of each of the three workloads the metric names,
+back to back on one stream:
+  * GQA g=4, 8B-shaped layer:  B=32, h_q=32, h_kv=8, D=128, T=4096, bf16
+  * GQA g=8, 70B-shaped layer: B=16, h_q=64, h_kv=8, D=128, ragged
+    seq_lens ~ U[1024, 32768] (seed 0), T_max=32768, bf16
+  * absorbed MLA, DeepSeek-V2-shaped layer: B=64, H=128, d_c=512, d_r=64,
+    T=4096, bf16 (when the MLA kernel is built)
+Each call is split into its two kernels (split-KV partial, log-sum-exp merge)
+with HIP events between them on the launch stream, so every kernel's time is
+measured live. ``value`` = KV-cache bytes of the step (valid positions only)
+divided by the wall time of a step. The MHA (Llama-2-7B layer) workload is
+timed separately and reported in ``config.breakdown`` only.
+
+Inputs are seeded synthetic tensors (``workloads``), resident in HBM before
+the timed region. The working set (> 1.6 GB per step) is far larger than the
+256 MB last-level cache, so every step streams the caches from HBM.
+
+The ``cpu_baseline`` leg times the fp64 oracle on a bounded sample of the
+same workloads on the host cores (rank 0, N=1 only).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- algorithmic work
+
+def gqa_work(w, lens):
+    """Bytes and FLOPs the method must move/do for one GQA decode step (valid positions only)."""
+    e = 2 if "bfloat16" in str(w.dtype) else 4
+    sum_n = int(sum(min(max(int(x), 0), w.T_max) for x in lens))
+    kv = 2 * w.h_kv * w.D * e * sum_n
+    q_out = 2 * w.B * w.h_q * w.D * e
+    flops = 4 * w.h_q * w.D * sum_n
+    return kv, q_out + 4 * w.B, flops
+
+
+def mla_work(w, lens):
+    sum_n = int(sum(min(max(int(x), 0), w.T_max) for x in lens))
+    kv = sum_n * (w.d_c + w.d_r) * 2
+    q_out = w.B * w.H * (w.d_c + w.d_r + w.d_c) * 2
+    flops = 2 * w.H * sum_n * ((w.d_c + w.d_r) + w.d_c)
+    return kv, q_out + 4 * w.B, flops
+
+
+# ----------------------------------------------------------------------------- traffic record
+
+def traffic_for(kernel_src: str, kernel_name: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if still valid for this source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    ent = rec.get(kernel_name)
+    if not ent or ent.get("source_sha256") != sha:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(items, budget_s=15.0):
+    """Time the fp64 oracle on whole sequences of each workload until the budget is spent."""
+    import numpy as np  # noqa: F401
+    import torch
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    done_bytes, t_used, parts = 0, 0.0, []
+    per = budget_s / max(1, len(items))
+    for name, kind, w, cpu in items:
+        t0 = time.perf_counter()
+        nseq = 0
+        for b in range(w.B):
+            if kind == "gqa":
+                q, k, v, lens = cpu
+                oracle.decode_gqa(q[b:b + 1], k[b:b + 1], v[b:b + 1], lens[b:b + 1], w.scale)
+                done_bytes += gqa_work(w, lens[b:b + 1])[0]
+            else:
+                qn, qr, lat, lens = cpu
+                oracle.decode_mla(qn[b:b + 1], qr[b:b + 1], lat[b:b + 1], lens[b:b + 1], w.scale, w.d_c)
+                done_bytes += mla_work(w, lens[b:b + 1])[0]
+            nseq += 1
+            if time.perf_counter() - t0 >= per:
+                break
+        dt = time.perf_counter() - t0
+        t_used += dt
+        parts.append(f"{name}: {nseq}/{w.B} sequences in {dt:.1f}s")
+    return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "sample": "; ".join(parts) +
+            " (fp64 oracle, whole sequences, KV bytes of the sampled sequences / time)"}
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--skip-mha", action="store_true", help="do not time the MHA breakdown workload")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library runs on a single MI355X and has no "
+              "multi-GPU path (see DESIGN.md for how it would shard). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import mla_kv_cache_amd as m
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    m.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    mla_ok = True
+    try:
+        m.attn_decode_mla_plan(W.MLA_V2.B, W.MLA_V2.H, W.MLA_V2.d_c, W.MLA_V2.d_r, W.MLA_V2.T_max)
+    except m.AttnError:
+        mla_ok = False
+
+    # ---- inputs (seeded, drawn on the host, copied once into HBM)
+    specs = [("gqa4", "gqa", W.GQA4_8B), ("gqa8", "gqa", W.GQA8_70B)]
+    if mla_ok:
+        specs.append(("mla", "mla", W.MLA_V2))
+    if not args.skip_mha:
+        specs.append(("mha7b", "gqa", W.MHA_7B))
+    items, cpu_items = [], []
+    for name, kind, w in specs:
+        t0 = time.perf_counter()
+        cpu = W.gqa_inputs(w) if kind == "gqa" else W.mla_inputs(w)
+        gpu = tuple(x.to(dev) for x in cpu)
+        log(f"[bench] inputs {name}: {time.perf_counter() - t0:.1f}s")
+        lens = cpu[3].tolist()
+        if kind == "gqa":
+            q, k, v, gl = gpu
+            P, NP, ws = m.attn_decode_gqa_plan(w.B, w.h_q, w.h_kv, w.D, w.T_max, w.dtype)
+            po = torch.empty((w.B, w.h_q, NP, w.D), dtype=torch.float32, device=dev)
+            pl = torch.empty((w.B, w.h_q, NP), dtype=torch.float32, device=dev)
+            out = torch.empty_like(q)
+            kv, other, flops = gqa_work(w, lens)
+
+            def partial(q=q, k=k, v=v, gl=gl, P=P, po=po, pl=pl, w=w):
+                m.attn_decode_gqa_partial(q, k, v, gl, P, scale=w.scale, part_out=po, part_lse=pl)
+
+            def merge(po=po, pl=pl, gl=gl, P=P, out=out, w=w):
+                m.attn_decode_merge(po, pl, gl, w.T_max, P, out=out)
+            kname = f"gqa_partial_kernel<BF16Elem, {w.D}, {w.group}>"
+            src = os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "gqa_decode.hip")
+        else:
+            qn, qr, lat, gl = gpu
+            P, NP, ws = m.attn_decode_mla_plan(w.B, w.H, w.d_c, w.d_r, w.T_max)
+            po = torch.empty((w.B, w.H, NP, w.d_c), dtype=torch.float32, device=dev)
+            pl = torch.empty((w.B, w.H, NP), dtype=torch.float32, device=dev)
+            out = torch.empty((w.B, w.H, w.d_c), dtype=torch.bfloat16, device=dev)
+            kv, other, flops = mla_work(w, lens)
+
+            def partial(qn=qn, qr=qr, lat=lat, gl=gl, P=P, po=po, pl=pl, w=w):
+                m.attn_decode_mla_partial(qn, qr, lat, gl, w.scale, P, part_out=po, part_lse=pl)
+
+            def merge(po=po, pl=pl, gl=gl, P=P, out=out, w=w):
+                m.attn_decode_merge(po, pl, gl, w.T_max, P, out=out)
+            kname = "mla_partial_kernel"
+            src = os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "mla_decode.hip")
+        items.append(dict(name=name, kind=kind, w=w, partial=partial, merge=merge, kv=kv,
+                          other=other, flops=flops, P=P, NP=NP, kname=kname, src=src,
+                          in_step=name != "mha7b"))
+        if name != "mha7b":
+            cpu_items.append((name, kind, w, cpu))
+        else:
+            del cpu
+    torch.cuda.synchronize()
+
+    step_items = [it for it in items if it["in_step"]]
+
+    def run_step(record=None):
+        for it in step_items:
+            if record is not None:
+                record[it["name"]][0].record(stream)
+            it["partial"]()
+            if record is not None:
+                record[it["name"]][1].record(stream)
+            it["merge"]()
+            if record is not None:
+                record[it["name"]][2].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    evs = [{it["name"]: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for it in step_items}
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run_step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    breakdown = {}
+    for it in step_items:
+        pt = [evs[s][it["name"]][0].elapsed_time(evs[s][it["name"]][1]) for s in range(args.steps)]
+        mt = [evs[s][it["name"]][1].elapsed_time(evs[s][it["name"]][2]) for s in range(args.steps)]
+        it["partial_ms"] = sum(pt) / len(pt)
+        it["merge_ms"] = sum(mt) / len(mt)
+        tot = it["partial_ms"] + it["merge_ms"]
+        breakdown[it["name"]] = {
+            "workload": it["w"].name, "partition_size": it["P"], "partitions": it["NP"],
+            "partial_us": round(it["partial_ms"] * 1e3, 2), "merge_us": round(it["merge_ms"] * 1e3, 2),
+            "kv_bytes": it["kv"], "kv_GBps": round(it["kv"] / (tot * 1e-3) / 1e9, 1),
+            "kv_frac_hbm_peak": round(it["kv"] / (tot * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "partial_kernel_GBps": round((it["kv"] + it["other"]) / (it["partial_ms"] * 1e-3) / 1e9, 1),
+        }
+        if it["kind"] == "mla":
+            tf = it["flops"] / (it["partial_ms"] * 1e-3) / 1e12
+            breakdown[it["name"]]["partial_TFLOPs"] = round(tf, 1)
+            breakdown[it["name"]]["mfma_frac_bf16_peak"] = round(tf / BF16_MFMA_PEAK_TFLOPS, 4)
+
+    # MHA breakdown: timed on its own, not part of the step.
+    for it in items:
+        if it["in_step"]:
+            continue
+        for _ in range(args.warmup):
+            it["partial"]()
+            it["merge"]()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        pts, mts = [], []
+        for _ in range(args.steps):
+            e[0].record(stream)
+            it["partial"]()
+            e[1].record(stream)
+            it["merge"]()
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            pts.append(e[0].elapsed_time(e[1]))
+            mts.append(e[1].elapsed_time(e[2]))
+        p_ms, m_ms = sum(pts) / len(pts), sum(mts) / len(mts)
+        breakdown[it["name"]] = {
+            "workload": it["w"].name, "partition_size": it["P"], "partitions": it["NP"],
+            "partial_us": round(p_ms * 1e3, 2), "merge_us": round(m_ms * 1e3, 2),
+            "kv_bytes": it["kv"], "kv_GBps": round(it["kv"] / ((p_ms + m_ms) * 1e-3) / 1e9, 1),
+            "kv_frac_hbm_peak": round(it["kv"] / ((p_ms + m_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "timed alone, not part of the step",
+        }
+
+    step_kv = sum(it["kv"] for it in step_items)
+    value = step_kv / (ms_per_step * 1e-3) / 1e9
+
+    dom = max(step_items, key=lambda it: it["partial_ms"])
+    achieved = (dom["kv"] + dom["other"]) / (dom["partial_ms"] * 1e-3) / 1e9
+    traffic = traffic_for(dom["src"], dom["kname"])
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dom["kname"], "workload": dom["w"].name,
+                "avg_launch_us": round(dom["partial_ms"] * 1e3, 2),
+                "algorithmic_bytes_per_launch": dom["kv"] + dom["other"]}
+
+    res = {
+        "metric": "KV-cache GB/s per decode step (GQA g=4, GQA g=8, MLA)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": " + ".join(it["w"].name for it in step_items),
+                   "step_kv_bytes": step_kv,
+                   "kv_frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+                   "decode_steps_per_s": round(1e3 / ms_per_step, 2),
+                   "breakdown": breakdown},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cpu_items, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * attn_decode.h -- C ABI of a decode-attention library for AMD MI355X (gfx950).
+ *
+ * One decode step: every sequence b of a batch has ONE new query token per
+ * head, and every query head attends over the n = seq_lens[b] positions
+ * already in its KV cache (the new token's own key/value included: the cache
+ * is appended first, then attended). There is no mask inside [0, n).
+ *
+ *   MHA / GQA / MQA   h_q query heads share h_kv KV heads in consecutive
+ *                     groups of g = h_q / h_kv: query head i reads KV head
+ *                     i / g (0-indexed; "Attention variants: MQA, GQA, and
+ *                     MLA", section "GQA: interpolating with groups", and
+ *                     "Grouped-Query Attention: Fewer KV Heads, Same
+ *                     Quality", section "Writing the formula explicitly").
+ *                     h_kv == h_q is MHA, h_kv == 1 is MQA.
+ *   absorbed MLA      H heads score against ONE cached row per token, the
+ *                     latent c (d_c values) followed by a decoupled rotary
+ *                     key (d_r values); the output of each head is the
+ *                     softmax-weighted average of the latents ("Attention
+ *                     variants: MQA, GQA, and MLA", section "MLA: cache a
+ *                     latent, not the keys and values").
+ *
+ * For each row (b, i):  s_t = scale * <q[b,i,:], K[b,j,t,:]>,  t < n
+ *                        out[b,i,:] = sum_t softmax(s)_t * V[b,j,t,:]
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor argument is a DEVICE pointer to contiguous row-major memory
+ *   with the shape written next to it. The caller owns all memory; the
+ *   library never allocates, frees or keeps a pointer after returning.
+ * - Work is enqueued asynchronously on `stream` (0 = the null stream). No
+ *   entry point synchronises the host. Results are ready when the stream
+ *   reaches the enqueued work.
+ * - Return value: ATTN_OK (0) or a negative attn_status. Every argument check
+ *   happens on the host BEFORE anything is enqueued; a non-zero return from
+ *   a check means nothing was launched. ATTN_ERR_HIP means a launch failed
+ *   (hipGetLastError); attn_status_str() names each code.
+ * - Device pointers must be 16-byte aligned (ATTN_ERR_UNSUPPORTED otherwise).
+ *   `out` must not overlap any input (ATTN_ERR_INVALID_ARG).
+ * - seq_lens: int32[B] on the device. A value is clamped to [0, T_max] in the
+ *   kernels; n == 0 yields an all-zero output row. Positions t >= n are
+ *   never read, so padding may hold any bits, NaN included.
+ * - Accumulation is fp32 whatever the storage type; out has q's dtype and is
+ *   rounded to nearest-even. Results are deterministic: same inputs and plan,
+ *   bit-identical output (no atomics, fixed reduction order).
+ * - Split-KV: positions are cut into partitions of `partition_size`; each
+ *   partition produces its softmax-normalised partial output and its log-sum-
+ *   exp, and a second kernel merges the partials. The *_partial / merge entry
+ *   points expose the two stages (for a caller that merges partials itself,
+ *   e.g. across devices); the one-call entry points run both with the
+ *   library's own partition size and a caller-provided workspace.
+ */
+#ifndef ATTN_DECODE_H
+#define ATTN_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = -1,  /* null pointer, non-positive size, h_q % h_kv != 0, overlap, overflow */
+  ATTN_ERR_UNSUPPORTED = -2,  /* valid but not built: head dim, group size, dtype, alignment */
+  ATTN_ERR_WORKSPACE = -3,    /* workspace pointer null or workspace_bytes too small */
+  ATTN_ERR_HIP = -4           /* a kernel launch reported an error */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* attn_status_str(int status);
+
+/* ---------------------------------------------------------------- cache-size helpers
+ * Exact host-only integer arithmetic; no device is touched.
+ *
+ * attn_kv_cache_bytes: bytes of K plus V, each [batch, n_kv_heads, seq_len,
+ * head_dim] per layer, i.e. 2 * n_layers * n_kv_heads * head_dim * seq_len *
+ * batch * bytes_per_elem ("Attention variants: MQA, GQA, and MLA", section
+ * "The KV cache bill, worked numerically"; same argument order as the page's
+ * helper, whose defaults are batch = 1 and bytes_per_elem = 2).
+ *
+ * attn_mla_cache_bytes: bytes of an MLA cache, one (d_c + d_r)-wide row per
+ * token per layer per sequence (same page, section "MLA: cache a latent, not
+ * the keys and values").
+ *
+ * Both return UINT64_MAX if the exact product does not fit in 64 bits.
+ */
+uint64_t attn_kv_cache_bytes(uint64_t n_layers, uint64_t n_kv_heads, uint64_t head_dim,
+                             uint64_t seq_len, uint64_t batch, uint64_t bytes_per_elem);
+uint64_t attn_mla_cache_bytes(uint64_t n_layers, uint64_t d_c, uint64_t d_r,
+                              uint64_t seq_len, uint64_t batch, uint64_t bytes_per_elem);
+
+/* ---------------------------------------------------------------- GQA / MHA / MQA
+ * q        [B, h_q, D]           dtype dt
+ * k_cache  [B, h_kv, T_max, D]   dtype dt
+ * v_cache  [B, h_kv, T_max, D]   dtype dt
+ * seq_lens int32 [B]
+ * out      [B, h_q, D]           dtype dt
+ * Supported: D in {64, 128}; g = h_q / h_kv in {1, 2, 4, 8, 16}; dt in
+ * {ATTN_F32, ATTN_BF16}. Any B >= 1, T_max >= 1 with B*h_kv*T_max*D < 2^40.
+ */
+
+/* The library's plan for a shape: partition size (positions per split),
+ * number of partitions ceil(T_max / partition_size), and the workspace bytes
+ * attn_decode_gqa needs. Outputs may be NULL. Returns a status. */
+int attn_decode_gqa_plan(int B, int h_q, int h_kv, int D, int T_max, attn_dtype dt,
+                         int* partition_size, int* num_partitions, size_t* workspace_bytes);
+
+/* Workspace bytes attn_decode_gqa needs for this shape; 0 if the shape is invalid
+ * or unsupported (every valid shape needs more than 0 bytes). */
+size_t attn_decode_gqa_workspace_bytes(int B, int h_q, int h_kv, int D, int T_max, attn_dtype dt);
+
+/* One decode step: split-KV partial kernel then log-sum-exp merge, both on
+ * `stream`. workspace: device memory of at least attn_decode_gqa_workspace_bytes
+ * bytes, 16-byte aligned, contents ignored on entry and clobbered. */
+int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* seq_lens, int B, int h_q, int h_kv, int D, int T_max,
+                    float scale, attn_dtype dt, void* out,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Stage 1 alone, with an explicit partition_size P >= 1 and NP = ceil(T_max / P):
+ * part_out [B, h_q, NP, D] fp32: softmax-weighted average of V over the valid
+ *          positions of partition p, i.e. t in [p*P, min((p+1)*P, n));
+ * part_lse [B, h_q, NP]    fp32: log2 of sum_t exp(s_t) over the same positions
+ *          (natural-exp scores, base-2 logarithm).
+ * Partitions with p*P >= n are not written (they hold no position). */
+int attn_decode_gqa_partial(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, int B, int h_q, int h_kv, int D, int T_max,
+                            float scale, attn_dtype dt, int partition_size,
+                            float* part_out, float* part_lse, hipStream_t stream);
+
+/* Stage 2: merge NP = ceil(T_max / partition_size) partials per row into
+ * out [B, H, Dv] (dtype out_dt), reading only the ceil(n / partition_size)
+ * partitions that hold positions: out = sum_p 2^(lse_p - M) part_out_p /
+ * sum_p 2^(lse_p - M) with M = max_p lse_p. Dv in {64, 128, 512} (a multiple of 4, at most 1024). */
+int attn_decode_merge(const float* part_out, const float* part_lse, const int32_t* seq_lens,
+                      int B, int H, int Dv, int T_max, int partition_size,
+                      attn_dtype out_dt, void* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------- absorbed MLA (bf16)
+ * q_nope_absorbed [B, H, d_c]          bf16: query times the key up-projection
+ * q_rope          [B, H, d_r]          bf16: query part for the rotary key
+ * latent_cache    [B, T_max, d_c+d_r]  bf16: [latent | rotary key] per token
+ * seq_lens        int32 [B]
+ * out             [B, H, d_c]          bf16: weighted average of latents
+ * s_t = scale * (<q_nope, latent[t, :d_c]> + <q_rope, latent[t, d_c:]>).
+ * Supported: (d_c, d_r) = (512, 64); H a multiple of 32 up to 128 (MFMA tiles of
+ * 32 heads); bf16 only. The rotary key is used as stored: rotating it and
+ * q_rope by position is the caller's job.
+ */
+int attn_decode_mla_plan(int B, int H, int d_c, int d_r, int T_max,
+                         int* partition_size, int* num_partitions, size_t* workspace_bytes);
+size_t attn_decode_mla_workspace_bytes(int B, int H, int d_c, int d_r, int T_max);
+
+int attn_decode_mla(const void* q_nope_absorbed, const void* q_rope, const void* latent_cache,
+                    const int32_t* seq_lens, int B, int H, int d_c, int d_r, int T_max,
+                    float scale, void* out, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/* Stage 1 alone; same partial layout as attn_decode_gqa_partial with h_q = H
+ * and D = d_c. Merge with attn_decode_merge(..., Dv = d_c, out_dt = ATTN_BF16). */
+int attn_decode_mla_partial(const void* q_nope_absorbed, const void* q_rope,
+                            const void* latent_cache, const int32_t* seq_lens,
+                            int B, int H, int d_c, int d_r, int T_max, float scale,
+                            int partition_size, float* part_out, float* part_lse,
+                            hipStream_t stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif /* ATTN_DECODE_H */

@@ -1,0 +1,239 @@
+"""Python binding of the MI355X decode-attention library (argument marshalling only).
+
+Every function has the name of the C entry point it calls (include/attn_decode.h)
+and takes torch tensors that already live on the GPU. The binding checks dtypes,
+shapes and contiguity, allocates outputs/workspaces when the caller passes none,
+and hands raw pointers plus torch's current HIP stream to the C library. All
+arithmetic runs in the HIP kernels; there is no CPU or PyTorch fallback, and a
+missing library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import ATTN_BF16, ATTN_F32, load
+
+__all__ = [
+    "AttnError", "load",
+    "attn_kv_cache_bytes", "attn_mla_cache_bytes",
+    "attn_decode_gqa_plan", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa",
+    "attn_decode_gqa_partial", "attn_decode_merge",
+    "attn_decode_mla_plan", "attn_decode_mla_workspace_bytes", "attn_decode_mla",
+    "attn_decode_mla_partial",
+]
+
+
+class AttnError(RuntimeError):
+    """A non-zero attn_status returned by the C library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        super().__init__(f"{where}: {_lib.status_str(status)} ({status})")
+
+
+def _check(st: int, where: str) -> None:
+    if st != _lib.ATTN_OK:
+        raise AttnError(st, where)
+
+
+_DT = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}: expected float32 or bfloat16")
+    return _DT[t.dtype]
+
+
+def _dev(*ts: torch.Tensor) -> torch.device:
+    dev = ts[0].device
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    return dev
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _lens(seq_lens: torch.Tensor, B: int) -> None:
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
+        raise ValueError(f"seq_lens must be int32 of shape ({B},)")
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def attn_kv_cache_bytes(n_layers: int, n_kv_heads: int, head_dim: int, seq_len: int,
+                        batch: int = 1, bytes_per_elem: int = 2) -> int:
+    """Exact KV-cache bytes: K and V, each [batch, kv_heads, seq, head_dim], per layer."""
+    return int(load().attn_kv_cache_bytes(n_layers, n_kv_heads, head_dim, seq_len, batch,
+                                          bytes_per_elem))
+
+
+def attn_mla_cache_bytes(n_layers: int, d_c: int, d_r: int, seq_len: int, batch: int = 1,
+                         bytes_per_elem: int = 2) -> int:
+    """Exact MLA cache bytes: one (d_c + d_r)-wide row per token per layer per sequence."""
+    return int(load().attn_mla_cache_bytes(n_layers, d_c, d_r, seq_len, batch, bytes_per_elem))
+
+
+def attn_decode_gqa_plan(B: int, h_q: int, h_kv: int, D: int, T_max: int, dtype=torch.bfloat16):
+    """(partition_size, num_partitions, workspace_bytes) the library picks for a shape."""
+    P, NP, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()
+    _check(load().attn_decode_gqa_plan(B, h_q, h_kv, D, T_max, _DT[dtype], ctypes.byref(P),
+                                       ctypes.byref(NP), ctypes.byref(ws)), "attn_decode_gqa_plan")
+    return P.value, NP.value, ws.value
+
+
+def attn_decode_gqa_workspace_bytes(B, h_q, h_kv, D, T_max, dtype=torch.bfloat16) -> int:
+    return int(load().attn_decode_gqa_workspace_bytes(B, h_q, h_kv, D, T_max, _DT[dtype]))
+
+
+def attn_decode_mla_plan(B: int, H: int, d_c: int, d_r: int, T_max: int):
+    P, NP, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()
+    _check(load().attn_decode_mla_plan(B, H, d_c, d_r, T_max, ctypes.byref(P), ctypes.byref(NP),
+                                       ctypes.byref(ws)), "attn_decode_mla_plan")
+    return P.value, NP.value, ws.value
+
+
+def attn_decode_mla_workspace_bytes(B, H, d_c, d_r, T_max) -> int:
+    return int(load().attn_decode_mla_workspace_bytes(B, H, d_c, d_r, T_max))
+
+
+# ----------------------------------------------------------------------------- GQA
+
+def _gqa_shapes(q, k_cache, v_cache):
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,h_q,D], k_cache and v_cache [B,h_kv,T_max,D]")
+    B, h_q, D = q.shape
+    if k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("q and k_cache disagree on B or D")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    return B, h_q, k_cache.shape[1], D, k_cache.shape[2]
+
+
+def attn_decode_gqa(q, k_cache, v_cache, seq_lens, scale: Optional[float] = None,
+                    out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """One decode step of MHA/GQA/MQA. Returns out [B, h_q, D] in q's dtype."""
+    B, h_q, h_kv, D, T_max = _gqa_shapes(q, k_cache, v_cache)
+    dev = _dev(q, k_cache, v_cache, seq_lens)
+    _lens(seq_lens, B)
+    dt = _dt(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    need = attn_decode_gqa_workspace_bytes(B, h_q, h_kv, D, T_max, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(out, workspace)
+    _check(load().attn_decode_gqa(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B, h_q,
+                                  h_kv, D, T_max, scale, dt, _ptr(out), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(dev)),
+           "attn_decode_gqa")
+    return out
+
+
+def attn_decode_gqa_partial(q, k_cache, v_cache, seq_lens, partition_size: int,
+                            scale: Optional[float] = None, part_out=None, part_lse=None):
+    """Stage 1 with an explicit partition size. Returns (part_out [B,h_q,NP,D], part_lse [B,h_q,NP])."""
+    B, h_q, h_kv, D, T_max = _gqa_shapes(q, k_cache, v_cache)
+    dev = _dev(q, k_cache, v_cache, seq_lens)
+    _lens(seq_lens, B)
+    NP = -(-T_max // int(partition_size)) if partition_size > 0 else 1
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if part_out is None:
+        part_out = torch.empty((B, h_q, NP, D), dtype=torch.float32, device=dev)
+    if part_lse is None:
+        part_lse = torch.empty((B, h_q, NP), dtype=torch.float32, device=dev)
+    _dev(part_out, part_lse)
+    _check(load().attn_decode_gqa_partial(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                          B, h_q, h_kv, D, T_max, scale, _dt(q), int(partition_size),
+                                          _ptr(part_out), _ptr(part_lse), _stream(dev)),
+           "attn_decode_gqa_partial")
+    return part_out, part_lse
+
+
+def attn_decode_merge(part_out, part_lse, seq_lens, T_max: int, partition_size: int,
+                      out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None):
+    """Stage 2: merge [B,H,NP,Dv] partials into out [B,H,Dv]."""
+    if part_out.dim() != 4 or part_lse.shape != part_out.shape[:3]:
+        raise ValueError("expected part_out [B,H,NP,Dv] and part_lse [B,H,NP]")
+    B, H, NP, Dv = part_out.shape
+    dev = _dev(part_out, part_lse, seq_lens)
+    _lens(seq_lens, B)
+    if NP != -(-int(T_max) // int(partition_size)):
+        raise ValueError("part_out's partition count does not match T_max / partition_size")
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=out_dtype, device=dev)
+    _dev(out)
+    _check(load().attn_decode_merge(_ptr(part_out), _ptr(part_lse), _ptr(seq_lens), B, H, Dv,
+                                    int(T_max), int(partition_size), _DT[out.dtype], _ptr(out),
+                                    _stream(dev)), "attn_decode_merge")
+    return out
+
+
+# ----------------------------------------------------------------------------- MLA
+
+def _mla_shapes(q_nope, q_rope, latent):
+    if q_nope.dim() != 3 or q_rope.dim() != 3 or latent.dim() != 3:
+        raise ValueError("expected q_nope [B,H,d_c], q_rope [B,H,d_r], latent [B,T_max,d_c+d_r]")
+    B, H, d_c = q_nope.shape
+    d_r = q_rope.shape[2]
+    if q_rope.shape[:2] != (B, H) or latent.shape[0] != B or latent.shape[2] != d_c + d_r:
+        raise ValueError("q_nope, q_rope and latent disagree on B, H or widths")
+    for t in (q_nope, q_rope, latent):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("MLA inputs must be bfloat16")
+    return B, H, d_c, d_r, latent.shape[1]
+
+
+def attn_decode_mla(q_nope_absorbed, q_rope, latent_cache, seq_lens, scale: float,
+                    out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """One absorbed-MLA decode step. Returns out [B, H, d_c] bf16."""
+    B, H, d_c, d_r, T_max = _mla_shapes(q_nope_absorbed, q_rope, latent_cache)
+    dev = _dev(q_nope_absorbed, q_rope, latent_cache, seq_lens)
+    _lens(seq_lens, B)
+    if out is None:
+        out = torch.empty((B, H, d_c), dtype=torch.bfloat16, device=dev)
+    need = attn_decode_mla_workspace_bytes(B, H, d_c, d_r, T_max)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(out, workspace)
+    _check(load().attn_decode_mla(_ptr(q_nope_absorbed), _ptr(q_rope), _ptr(latent_cache),
+                                  _ptr(seq_lens), B, H, d_c, d_r, T_max, float(scale), _ptr(out),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(dev)), "attn_decode_mla")
+    return out
+
+
+def attn_decode_mla_partial(q_nope_absorbed, q_rope, latent_cache, seq_lens, scale: float,
+                            partition_size: int, part_out=None, part_lse=None):
+    B, H, d_c, d_r, T_max = _mla_shapes(q_nope_absorbed, q_rope, latent_cache)
+    dev = _dev(q_nope_absorbed, q_rope, latent_cache, seq_lens)
+    _lens(seq_lens, B)
+    NP = -(-T_max // int(partition_size)) if partition_size > 0 else 1
+    if part_out is None:
+        part_out = torch.empty((B, H, NP, d_c), dtype=torch.float32, device=dev)
+    if part_lse is None:
+        part_lse = torch.empty((B, H, NP), dtype=torch.float32, device=dev)
+    _dev(part_out, part_lse)
+    _check(load().attn_decode_mla_partial(_ptr(q_nope_absorbed), _ptr(q_rope), _ptr(latent_cache),
+                                          _ptr(seq_lens), B, H, d_c, d_r, T_max, float(scale),
+                                          int(partition_size), _ptr(part_out), _ptr(part_lse),
+                                          _stream(dev)), "attn_decode_mla_partial")
+    return part_out, part_lse

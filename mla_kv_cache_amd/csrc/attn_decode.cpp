@@ -1,0 +1,329 @@
+// Host side of the C ABI declared in include/attn_decode.h: argument checks,
+// the split-KV plan, workspace layout and kernel dispatch. Every check runs
+// before anything is enqueued; nothing here allocates or synchronises.
+
+#include "attn_decode.h"
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;        // start of each workspace region
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int kMaxTmax = 1 << 30;
+constexpr int kMaxGridYZ = 65535;
+constexpr double kLog2e = 1.4426950408889634074;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+int elem_size(attn_dtype dt) { return dt == ATTN_BF16 ? 2 : 4; }
+
+int ceil_div(int a, int b) { return a / b + (a % b != 0); }
+
+// Exact a*b in uint64, saturating at UINT64_MAX.
+uint64_t mul_sat(uint64_t a, uint64_t b) {
+  if (a == 0 || b == 0) return 0;
+  if (a > UINT64_MAX / b) return UINT64_MAX;
+  return a * b;
+}
+
+// ------------------------------------------------------------------ GQA plan
+
+struct GqaShape {
+  int B, h_q, h_kv, D, T_max;
+  attn_dtype dt;
+};
+
+int check_gqa_shape(const GqaShape& s) {
+  if (s.B < 1 || s.h_q < 1 || s.h_kv < 1 || s.D < 1 || s.T_max < 1) return ATTN_ERR_INVALID_ARG;
+  if (s.h_q % s.h_kv != 0) return ATTN_ERR_INVALID_ARG;
+  if (s.T_max > kMaxTmax || s.B > kMaxGridYZ || s.h_kv > kMaxGridYZ) return ATTN_ERR_INVALID_ARG;
+  if (int64_t(s.B) * s.h_kv * s.T_max * s.D >= kMaxElems) return ATTN_ERR_INVALID_ARG;
+  if (int64_t(s.B) * s.h_q >= (int64_t(1) << 31)) return ATTN_ERR_INVALID_ARG;
+  if (s.dt != ATTN_F32 && s.dt != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!attn::gqa_supported(int(s.dt), s.D, s.h_q / s.h_kv)) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+// Positions per partition: a power of two in [256, 4096] chosen so that the
+// (b, kv head, partition) grid holds about 2048 work-groups (8 per CU on the
+// 256-CU part) when the cache is full.
+int gqa_auto_partition(const GqaShape& s) {
+  const int64_t pairs = int64_t(s.B) * s.h_kv;
+  const int64_t want = (int64_t(s.T_max) * pairs + 2047) / 2048;
+  int P = 256;
+  while (P < want && P < 4096) P <<= 1;
+  return P;
+}
+
+size_t partial_bytes(int64_t rows, int NP, int Dv) {
+  return align_up(size_t(rows) * NP * Dv * sizeof(float)) + align_up(size_t(rows) * NP * sizeof(float));
+}
+
+// ------------------------------------------------------------------ MLA plan
+
+struct MlaShape {
+  int B, H, d_c, d_r, T_max;
+};
+
+int check_mla_shape(const MlaShape& s) {
+  if (s.B < 1 || s.H < 1 || s.d_c < 1 || s.d_r < 0 || s.T_max < 1) return ATTN_ERR_INVALID_ARG;
+  if (s.T_max > kMaxTmax || s.B > kMaxGridYZ) return ATTN_ERR_INVALID_ARG;
+  if (int64_t(s.B) * s.T_max * (s.d_c + s.d_r) >= kMaxElems) return ATTN_ERR_INVALID_ARG;
+  if (!attn::mla_supported(s.H, s.d_c, s.d_r)) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+// Positions per partition for MLA: a work-group holds all heads of one
+// sequence, so the grid is B x partitions; aim for about 256 work-groups
+// (one per CU) with partitions of at least 256 positions.
+int mla_auto_partition(const MlaShape& s) {
+  const int64_t want = (int64_t(s.T_max) * s.B + 255) / 256;
+  int P = 256;
+  while (P < want && P < (1 << 20)) P <<= 1;
+  return P;
+}
+
+int set_plan(int P, int T_max, size_t ws, int* partition_size, int* num_partitions,
+             size_t* workspace_bytes) {
+  if (partition_size) *partition_size = P;
+  if (num_partitions) *num_partitions = ceil_div(T_max, P);
+  if (workspace_bytes) *workspace_bytes = ws;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: shape, dtype or alignment not supported";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace missing or too small";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP: kernel launch failed";
+    default: return "unknown attn_status";
+  }
+}
+
+uint64_t attn_kv_cache_bytes(uint64_t n_layers, uint64_t n_kv_heads, uint64_t head_dim,
+                             uint64_t seq_len, uint64_t batch, uint64_t bytes_per_elem) {
+  uint64_t x = mul_sat(2, n_layers);
+  x = mul_sat(x, n_kv_heads);
+  x = mul_sat(x, head_dim);
+  x = mul_sat(x, seq_len);
+  x = mul_sat(x, batch);
+  return mul_sat(x, bytes_per_elem);
+}
+
+uint64_t attn_mla_cache_bytes(uint64_t n_layers, uint64_t d_c, uint64_t d_r, uint64_t seq_len,
+                              uint64_t batch, uint64_t bytes_per_elem) {
+  if (d_c > UINT64_MAX - d_r) return UINT64_MAX;
+  uint64_t x = mul_sat(n_layers, d_c + d_r);
+  x = mul_sat(x, seq_len);
+  x = mul_sat(x, batch);
+  return mul_sat(x, bytes_per_elem);
+}
+
+// ------------------------------------------------------------------ GQA
+
+int attn_decode_gqa_plan(int B, int h_q, int h_kv, int D, int T_max, attn_dtype dt,
+                         int* partition_size, int* num_partitions, size_t* workspace_bytes) {
+  const GqaShape s{B, h_q, h_kv, D, T_max, dt};
+  const int st = check_gqa_shape(s);
+  if (st != ATTN_OK) return st;
+  const int P = gqa_auto_partition(s);
+  const int NP = ceil_div(T_max, P);
+  return set_plan(P, T_max, partial_bytes(int64_t(B) * h_q, NP, D), partition_size,
+                  num_partitions, workspace_bytes);
+}
+
+size_t attn_decode_gqa_workspace_bytes(int B, int h_q, int h_kv, int D, int T_max, attn_dtype dt) {
+  size_t ws = 0;
+  if (attn_decode_gqa_plan(B, h_q, h_kv, D, T_max, dt, nullptr, nullptr, &ws) != ATTN_OK) return 0;
+  return ws;
+}
+
+static int check_gqa_ptrs(const GqaShape& s, const void* q, const void* k, const void* v,
+                          const int32_t* lens, const void* out, size_t out_bytes) {
+  if (!q || !k || !v || !lens || !out) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_UNSUPPORTED;
+  const size_t es = elem_size(s.dt);
+  const size_t qb = size_t(s.B) * s.h_q * s.D * es;
+  const size_t kb = size_t(s.B) * s.h_kv * size_t(s.T_max) * s.D * es;
+  if (overlap(out, out_bytes, q, qb) || overlap(out, out_bytes, k, kb) ||
+      overlap(out, out_bytes, v, kb) || overlap(out, out_bytes, lens, size_t(s.B) * 4))
+    return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+int attn_decode_gqa_partial(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, int B, int h_q, int h_kv, int D, int T_max,
+                            float scale, attn_dtype dt, int partition_size, float* part_out,
+                            float* part_lse, hipStream_t stream) {
+  const GqaShape s{B, h_q, h_kv, D, T_max, dt};
+  int st = check_gqa_shape(s);
+  if (st != ATTN_OK) return st;
+  if (partition_size < 1 || !isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  const int NP = ceil_div(T_max, partition_size);
+  const size_t ob = size_t(B) * h_q * NP * D * sizeof(float);
+  st = check_gqa_ptrs(s, q, k_cache, v_cache, seq_lens, part_out, ob);
+  if (st != ATTN_OK) return st;
+  if (!part_lse) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(part_lse)) return ATTN_ERR_UNSUPPORTED;
+  if (overlap(part_out, ob, part_lse, size_t(B) * h_q * NP * sizeof(float))) return ATTN_ERR_INVALID_ARG;
+  const float sc = float(double(scale) * kLog2e);
+  if (attn::launch_gqa_partial(int(dt), D, h_q / h_kv, q, k_cache, v_cache, seq_lens, B, h_kv,
+                               T_max, partition_size, NP, sc, part_out, part_lse,
+                               stream) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+int attn_decode_merge(const float* part_out, const float* part_lse, const int32_t* seq_lens,
+                      int B, int H, int Dv, int T_max, int partition_size, attn_dtype out_dt,
+                      void* out, hipStream_t stream) {
+  if (B < 1 || H < 1 || Dv < 1 || T_max < 1 || partition_size < 1) return ATTN_ERR_INVALID_ARG;
+  if (T_max > kMaxTmax || int64_t(B) * H >= (int64_t(1) << 31)) return ATTN_ERR_INVALID_ARG;
+  if (!part_out || !part_lse || !seq_lens || !out) return ATTN_ERR_INVALID_ARG;
+  if (!attn::merge_supported(int(out_dt), Dv)) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(part_out) || !aligned16(part_lse) || !aligned16(out)) return ATTN_ERR_UNSUPPORTED;
+  const int NP = ceil_div(T_max, partition_size);
+  const size_t rows = size_t(B) * H;
+  const size_t out_b = rows * Dv * elem_size(out_dt);
+  if (overlap(out, out_b, part_out, rows * NP * Dv * sizeof(float)) ||
+      overlap(out, out_b, part_lse, rows * NP * sizeof(float)))
+    return ATTN_ERR_INVALID_ARG;
+  if (attn::launch_merge(int(out_dt), part_out, part_lse, seq_lens, B, H, Dv, T_max,
+                         partition_size, NP, out, stream) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* seq_lens, int B, int h_q, int h_kv, int D, int T_max,
+                    float scale, attn_dtype dt, void* out, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  const GqaShape s{B, h_q, h_kv, D, T_max, dt};
+  int st = check_gqa_shape(s);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  const size_t out_b = size_t(B) * h_q * D * elem_size(dt);
+  st = check_gqa_ptrs(s, q, k_cache, v_cache, seq_lens, out, out_b);
+  if (st != ATTN_OK) return st;
+  const int P = gqa_auto_partition(s);
+  const int NP = ceil_div(T_max, P);
+  const size_t need = partial_bytes(int64_t(B) * h_q, NP, D);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
+  if (overlap(workspace, need, out, out_b)) return ATTN_ERR_INVALID_ARG;
+  float* part_out = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             align_up(size_t(B) * h_q * NP * D * sizeof(float)));
+  const float sc = float(double(scale) * kLog2e);
+  if (attn::launch_gqa_partial(int(dt), D, h_q / h_kv, q, k_cache, v_cache, seq_lens, B, h_kv,
+                               T_max, P, NP, sc, part_out, part_lse, stream) != hipSuccess)
+    return ATTN_ERR_HIP;
+  if (attn::launch_merge(int(dt), part_out, part_lse, seq_lens, B, h_q, D, T_max, P, NP, out,
+                         stream) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+// ------------------------------------------------------------------ MLA
+
+int attn_decode_mla_plan(int B, int H, int d_c, int d_r, int T_max, int* partition_size,
+                         int* num_partitions, size_t* workspace_bytes) {
+  const MlaShape s{B, H, d_c, d_r, T_max};
+  const int st = check_mla_shape(s);
+  if (st != ATTN_OK) return st;
+  const int P = mla_auto_partition(s);
+  const int NP = ceil_div(T_max, P);
+  return set_plan(P, T_max, partial_bytes(int64_t(B) * H, NP, d_c), partition_size,
+                  num_partitions, workspace_bytes);
+}
+
+size_t attn_decode_mla_workspace_bytes(int B, int H, int d_c, int d_r, int T_max) {
+  size_t ws = 0;
+  if (attn_decode_mla_plan(B, H, d_c, d_r, T_max, nullptr, nullptr, &ws) != ATTN_OK) return 0;
+  return ws;
+}
+
+static int check_mla_ptrs(const MlaShape& s, const void* qn, const void* qr, const void* lat,
+                          const int32_t* lens, const void* out, size_t out_bytes) {
+  if (!qn || !qr || !lat || !lens || !out) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(qn) || !aligned16(qr) || !aligned16(lat) || !aligned16(out))
+    return ATTN_ERR_UNSUPPORTED;
+  const size_t qnb = size_t(s.B) * s.H * s.d_c * 2, qrb = size_t(s.B) * s.H * s.d_r * 2;
+  const size_t lb = size_t(s.B) * size_t(s.T_max) * (s.d_c + s.d_r) * 2;
+  if (overlap(out, out_bytes, qn, qnb) || overlap(out, out_bytes, qr, qrb) ||
+      overlap(out, out_bytes, lat, lb) || overlap(out, out_bytes, lens, size_t(s.B) * 4))
+    return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+int attn_decode_mla_partial(const void* q_nope, const void* q_rope, const void* latent,
+                            const int32_t* seq_lens, int B, int H, int d_c, int d_r, int T_max,
+                            float scale, int partition_size, float* part_out, float* part_lse,
+                            hipStream_t stream) {
+  const MlaShape s{B, H, d_c, d_r, T_max};
+  int st = check_mla_shape(s);
+  if (st != ATTN_OK) return st;
+  if (partition_size < 1 || !isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  const int NP = ceil_div(T_max, partition_size);
+  const size_t ob = size_t(B) * H * NP * d_c * sizeof(float);
+  st = check_mla_ptrs(s, q_nope, q_rope, latent, seq_lens, part_out, ob);
+  if (st != ATTN_OK) return st;
+  if (!part_lse) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(part_lse)) return ATTN_ERR_UNSUPPORTED;
+  if (overlap(part_out, ob, part_lse, size_t(B) * H * NP * sizeof(float))) return ATTN_ERR_INVALID_ARG;
+  const float sc = float(double(scale) * kLog2e);
+  if (attn::launch_mla_partial(q_nope, q_rope, latent, seq_lens, B, H, T_max, partition_size, NP,
+                               sc, part_out, part_lse, stream) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+int attn_decode_mla(const void* q_nope, const void* q_rope, const void* latent,
+                    const int32_t* seq_lens, int B, int H, int d_c, int d_r, int T_max,
+                    float scale, void* out, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  const MlaShape s{B, H, d_c, d_r, T_max};
+  int st = check_mla_shape(s);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  const size_t out_b = size_t(B) * H * d_c * 2;
+  st = check_mla_ptrs(s, q_nope, q_rope, latent, seq_lens, out, out_b);
+  if (st != ATTN_OK) return st;
+  const int P = mla_auto_partition(s);
+  const int NP = ceil_div(T_max, P);
+  const size_t need = partial_bytes(int64_t(B) * H, NP, d_c);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
+  if (overlap(workspace, need, out, out_b)) return ATTN_ERR_INVALID_ARG;
+  float* part_out = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             align_up(size_t(B) * H * NP * d_c * sizeof(float)));
+  const float sc = float(double(scale) * kLog2e);
+  if (attn::launch_mla_partial(q_nope, q_rope, latent, seq_lens, B, H, T_max, P, NP, sc, part_out,
+                               part_lse, stream) != hipSuccess)
+    return ATTN_ERR_HIP;
+  if (attn::launch_merge(int(ATTN_BF16), part_out, part_lse, seq_lens, B, H, d_c, T_max, P, NP,
+                         out, stream) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+}  // extern "C"

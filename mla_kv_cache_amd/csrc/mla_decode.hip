@@ -1,0 +1,305 @@
+// Absorbed multi-head latent attention, split-KV decode, on gfx950 MFMA.
+//
+// After the key up-projection is absorbed into the query, every head scores
+// against the SAME cached row per token (latent c of d_c = 512 values, then
+// a decoupled rotary key of d_r = 64 values) and averages the latents
+// ("Attention variants: MQA, GQA, and MLA", section "MLA: cache a latent,
+// not the keys and values"). Many heads share one wide row, so the two
+// products are dense contractions and run on the matrix cores:
+//
+//   S^T [32 positions x 32 heads]  = L_tile [32 x 576] . Q^T [576 x 32]
+//   O^T [512 dims x 32 heads]     += L_tile^T [512 x 32] . P^T [32 x 32]
+//
+// One work-group owns (sequence b, head block of up to 128 heads, partition
+// p) and runs two waves per 32 heads (8 waves for 128 heads, two per SIMD).
+// The two waves of a pair split the 576-wide score contraction in halves,
+// exchange their fp32 partial scores through LDS and add them in a fixed
+// order (both then hold the same scores and the same softmax state), and
+// split the 512 output dims in halves. Per wave that leaves 18 query
+// fragments and 8 output tiles resident in registers for the partition.
+//
+// The latent tile (32 positions x 576, padded to a 1168-byte row stride so
+// that both read patterns below are free of bank conflicts) is copied from
+// HBM straight into LDS with global_load_lds (no register staging), double
+// buffered: the copy of tile i+1 is in flight while tile i is computed. HBM
+// sees every cached row of the partition once.
+//
+// MFMA 32x32x16 bf16 operand layout (lane l): A[m][k] holds m = l % 32,
+// k = 8*(l/32) + j; B[k][n] holds n = l % 32, k = 8*(l/32) + j; result
+// register r holds row 8*(r/4) + 4*(l/32) + r%4, column l % 32. So in S^T
+// and O^T every lane works for exactly one head (l % 32): the softmax state
+// is lane-local apart from one exchange with lane l ^ 32, which holds the
+// other 16 positions of the same head.
+//
+// P^T enters the second product as the B operand straight from the S^T
+// result registers: over the positions the contraction index may be
+// permuted, provided A uses the same order, and A = L^T is read with the
+// LDS transpose load (ds_read_b64_tr_b16), whose 16-lane groups deliver
+// lane i, slot j from source lane 4j + i/4, slot i%4.
+//
+// The weights enter the second product as a pair of bf16 values hi + lo
+// (two MFMAs on the same latent fragment), so they carry about 16 significant
+// bits instead of bf16's 8; accumulation is fp32 throughout. Online softmax in the exp2 domain with the same lazy
+// rescale rule as the GQA kernel (only when a tile's maximum exceeds the
+// running one by more than 8).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_util.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kDc = 512;
+constexpr int kDr = 64;
+constexpr int kRow = kDc + kDr;            // 576 bf16 per cached token
+constexpr int kTile = 32;                  // positions per tile
+constexpr int kStride = kRow + 8;          // LDS row stride in bf16 (1168 bytes)
+constexpr int kSteps = kRow / 16;          // 36 k-steps of the score product
+constexpr int kOTiles = kDc / 32;          // 16 output tiles of 32 latent dims
+constexpr int kChunks = kTile * kRow / 8;  // 16-byte chunks per tile (2304)
+constexpr float kTau = 8.0f;
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+}
+__device__ __forceinline__ float bf16_round(float a) {
+  return __uint_as_float((uint32_t)f32_to_bf16_rne(a) << 16);
+}
+
+constexpr int kRowChunks = kStride / 8;               // 73 16-byte chunks per LDS row (72 + pad)
+constexpr int kBufBytes = (kTile * kStride * 2 + 1023) / 1024 * 1024;  // 37888: whole 1 KiB copy blocks
+constexpr int kBlocks = kBufBytes / 1024;                // 37 wave-wide copies per tile
+constexpr int kHalfSteps = kSteps / 2;                   // 18 score k-steps per wave
+constexpr int kHalfTiles = kOTiles / 2;                  // 8 output tiles per wave
+
+// Copy one latent tile (positions [t0, t0+32), rows past `end` replaced by row
+// end-1) into an LDS buffer. Each wave copies whole 1 KiB blocks: lane i of
+// block k fills LDS chunk 64k + i; pad chunks and the slack past the tile
+// receive a harmless in-bounds row.
+//
+// The copy is issued as global_load_lds_dwordx4 in inline assembly: it writes
+// no register, only LDS, and M0 holds the block's LDS address (no other code
+// in these kernels uses M0). Written this way the compiler does not insert a
+// wait for the copy before every later LDS read (it cannot prove that the
+// reads touch the other buffer); the kernel waits for the copy itself
+// (s_waitcnt vmcnt(0) before the barrier that opens the next tile).
+template <int NWAVES>
+__device__ __forceinline__ void copy_tile(unsigned char* buf, const uint16_t* lat_b, int t0, int end,
+                                          int wave, int lane) {
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)buf;
+  for (int blk = wave; blk < kBlocks; blk += NWAVES) {
+    const int ci = 64 * blk + lane;
+    const int row = ci / kRowChunks, c16 = ci % kRowChunks;
+    const bool data = row < kTile && c16 < kRow / 8;
+    const int grow = min(t0 + (data ? row : 0), end - 1);
+    const uint16_t* src = lat_b + (size_t)grow * kRow + (data ? c16 * 8 : 0);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + 1024u * (uint32_t)blk);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "memory");
+  }
+}
+
+template <int NHB>
+__global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
+    const uint16_t* __restrict__ lat, const int32_t* __restrict__ seq_lens, int H, int T_max,
+    int P, int NP, float qk_scale_log2, float* __restrict__ part_out,
+    float* __restrict__ part_lse) {
+  constexpr int NWAVES = 2 * NHB;
+  // Two tile buffers as separate objects: the compiler can then tell the copy
+  // into one from the reads of the other and does not wait for the copy.
+  __shared__ __attribute__((aligned(1024))) unsigned char buf0[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf1[kBufBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char xbuf[NWAVES * 4096];
+
+  const int p = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;
+  const int n = min(max(seq_lens[b], 0), T_max);
+  const int start = p * P;
+  if (start >= n) return;
+  const int end = min(start, n - P) + P;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kh = wave & 1;             // half of the contraction / of the output dims
+  const int half = lane >> 5;          // which 16 of a tile's 32 positions this lane holds
+  const int col = lane & 31;           // this lane's head within the pair's 32
+  const int head = hb * (32 * NHB) + (wave >> 1) * 32 + col;
+
+  // Query fragments for this wave's half of the 576 score dims.
+  uint4 qf[kHalfSteps];
+  {
+    const uint16_t* qn = q_nope + ((size_t)b * H + head) * kDc;
+    const uint16_t* qr = q_rope + ((size_t)b * H + head) * kDr;
+#pragma unroll
+    for (int ks = 0; ks < kHalfSteps; ++ks) {
+      const int d = 16 * (kHalfSteps * kh + ks) + 8 * half;
+      qf[ks] = d < kDc ? ld16(qn + d) : ld16(qr + (d - kDc));
+    }
+  }
+
+  f32x16 acc[kHalfTiles];
+#pragma unroll
+  for (int t = 0; t < kHalfTiles; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  float m = kNegInf, lsum = 0.f;
+
+  const uint16_t* lat_b = lat + (size_t)b * T_max * kRow;
+  // LDS transpose-read addressing, constant per lane (see the file comment).
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int tr_row = 4 * (g16 >> 1) + (i16 >> 2);
+  const int tr_col = 256 * kh + 16 * (g16 & 1) + 4 * (i16 & 3);
+
+  // One tile: wait for its copy, start the next copy into the other buffer,
+  // then scores, exchange, softmax and the output product.
+  auto tile = [&](const unsigned char* __restrict__ cur_b, unsigned char* __restrict__ nxt_b, int t0) {
+    const uint16_t* cur = reinterpret_cast<const uint16_t*>(cur_b);
+    // This wave's copies of this tile have landed; after the barrier everyone's
+    // have, and every wave is done with the other buffer.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t0 + kTile < end) copy_tile<NWAVES>(nxt_b, lat_b, t0 + kTile, end, wave, lane);
+
+    // ---- partial scores over this wave's 288 dims: S^T = L . Q^T
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    const uint16_t* arow = cur + col * kStride + 16 * kHalfSteps * kh + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < kHalfSteps; ++ks) {
+      const uint4 a = *reinterpret_cast<const uint4*>(arow + 16 * ks);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, qf[ks]), s, 0, 0, 0);
+    }
+    // ---- exchange with the partner wave; add in the fixed order (half 0) + (half 1)
+    {
+      float4* mine = reinterpret_cast<float4*>(xbuf + wave * 4096) + lane;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) mine[64 * g] = make_float4(s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]);
+      // LDS writes done, then a plain barrier: no release fence, which would
+      // also wait for the copy of the next tile that is in flight.
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const float4* other = reinterpret_cast<const float4*>(xbuf + (wave ^ 1) * 4096) + lane;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 o = other[64 * g];
+        const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[4 * g + e] = kh == 0 ? s[4 * g + e] + ov[e] : ov[e] + s[4 * g + e];
+      }
+    }
+
+    // ---- online softmax for head `col` over this tile's positions
+    float x[16];
+    float mt = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int pos = t0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      x[r] = pos < end ? s[r] * qk_scale_log2 : kNegInf;
+      mt = fmaxf(mt, x[r]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const bool need = mt > m + kTau;
+    if (__any(need)) {
+      const float f = need ? fast_exp2(m - mt) : 1.f;
+      m = need ? mt : m;
+      lsum *= f;
+#pragma unroll
+      for (int t = 0; t < kHalfTiles; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] *= f;
+    }
+    // Weights as a bf16 pair hi + lo (hi = bf16(p), lo = bf16(p - hi)): the
+    // product below runs once per part on the same latent fragment, so the
+    // weights enter with ~2^-17 relative error instead of bf16's 2^-9.
+    float pr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pr[r] = x[r] == kNegInf ? 0.f : fast_exp2(x[r] - m);
+      lsum += pr[r];
+    }
+
+    // ---- O^T += L^T . P^T over this wave's 256 output dims (two k-steps of 16 positions)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = pr[8 * ks + 2 * e], p1 = pr[8 * ks + 2 * e + 1];
+        const float h0 = bf16_round(p0), h1 = bf16_round(p1);
+        ph[e] = pack_bf16(h0, h1);
+        pl[e] = pack_bf16(p0 - h0, p1 - h1);
+      }
+      const bf16x8 pbh = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+      const bf16x8 pbl = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+      const uint16_t* base = cur + (16 * ks + tr_row) * kStride + tr_col;
+#pragma unroll
+      for (int t = 0; t < kHalfTiles; ++t) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 32 * t));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * kStride + 32 * t));
+        uint4 a;
+        a.x = __builtin_bit_cast(uint2, lo).x;
+        a.y = __builtin_bit_cast(uint2, lo).y;
+        a.z = __builtin_bit_cast(uint2, hi).x;
+        a.w = __builtin_bit_cast(uint2, hi).y;
+        const bf16x8 av = __builtin_bit_cast(bf16x8, a);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbh, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbl, acc[t], 0, 0, 0);
+      }
+    }
+  };
+
+  copy_tile<NWAVES>(buf0, lat_b, start, end, wave, lane);
+  for (int t0 = start;;) {
+    tile(buf0, buf1, t0);
+    if ((t0 += kTile) >= end) break;
+    tile(buf1, buf0, t0);
+    if ((t0 += kTile) >= end) break;
+  }
+
+  // Lanes l and l^32 share a head and a running maximum; add their sums.
+  lsum += __shfl_xor(lsum, 32, 64);
+  const float inv = 1.f / lsum;
+  const size_t prow = ((size_t)b * H + head) * NP + p;
+  float* po = part_out + prow * kDc + 256 * kh;
+#pragma unroll
+  for (int t = 0; t < kHalfTiles; ++t) {
+#pragma unroll
+    for (int r = 0; r < 16; r += 4) {
+      const int d = 32 * t + 8 * (r >> 2) + 4 * half;
+      *reinterpret_cast<float4*>(po + d) =
+          make_float4(acc[t][r] * inv, acc[t][r + 1] * inv, acc[t][r + 2] * inv, acc[t][r + 3] * inv);
+    }
+  }
+  if (kh == 0 && half == 0) part_lse[prow] = m + fast_log2(lsum);
+}
+
+}  // namespace
+
+bool mla_supported(int H, int d_c, int d_r) {
+  return d_c == kDc && d_r == kDr && H >= 32 && H % 32 == 0 && (H <= 128 || H % 128 == 0);
+}
+
+hipError_t launch_mla_partial(const void* q_nope, const void* q_rope, const void* latent,
+                              const int32_t* seq_lens, int B, int H, int T_max, int P, int NP,
+                              float sc, float* part_out, float* part_lse, hipStream_t stream) {
+  const int nhb = H >= 128 ? 4 : H / 32;  // 32-head blocks per work-group
+  const dim3 grid(NP, H / (32 * nhb), B);
+  const auto* qn = static_cast<const uint16_t*>(q_nope);
+  const auto* qr = static_cast<const uint16_t*>(q_rope);
+  const auto* lt = static_cast<const uint16_t*>(latent);
+  switch (nhb) {
+    case 4: hipLaunchKernelGGL(mla_partial_kernel<4>, grid, dim3(512), 0, stream, qn, qr, lt, seq_lens, H, T_max, P, NP, sc, part_out, part_lse); break;
+    case 3: hipLaunchKernelGGL(mla_partial_kernel<3>, grid, dim3(384), 0, stream, qn, qr, lt, seq_lens, H, T_max, P, NP, sc, part_out, part_lse); break;
+    case 2: hipLaunchKernelGGL(mla_partial_kernel<2>, grid, dim3(256), 0, stream, qn, qr, lt, seq_lens, H, T_max, P, NP, sc, part_out, part_lse); break;
+    default: hipLaunchKernelGGL(mla_partial_kernel<1>, grid, dim3(128), 0, stream, qn, qr, lt, seq_lens, H, T_max, P, NP, sc, part_out, part_lse); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attn

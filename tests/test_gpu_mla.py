@@ -1,0 +1,161 @@
+"""GPU parity of the absorbed-MLA decode path against the fp64 oracle.
+
+Tolerances as for the GQA path: bf16 inputs, fp32 accumulation -> max-abs 2e-3
+for fp32-written results (partial kernel + merge in fp32), plus half a bf16
+ulp of the oracle value when the result itself is bf16. Bit-exact: one cached
+position returns its latent, NaN padding is never read, repeated runs agree.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _m():
+    import mla_kv_cache_amd as m
+    return m
+
+
+def _half_ulp_bf16(x):
+    a = np.abs(x)
+    return 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -126))) - 8)
+
+
+def _f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def _inputs(w, dev, seq_lens=None):
+    qn, qr, lat, lens = W.mla_inputs(w, seq_lens=seq_lens)
+    return (qn, qr, lat, lens), (qn.to(dev), qr.to(dev), lat.to(dev), lens.to(dev))
+
+
+def _fp32_out(m, gqn, gqr, glat, gl, scale, P):
+    po, pl = m.attn_decode_mla_partial(gqn, gqr, glat, gl, scale, P)
+    return m.attn_decode_merge(po, pl, gl, glat.shape[1], P, out_dtype=torch.float32)
+
+
+CASES = [
+    # (B, H, T_max, lens)
+    (2, 128, 600, [600, 333]),
+    (3, 128, 1000, [1, 999, 64]),
+    (2, 64, 300, [300, 31]),
+    (2, 32, 257, [257, 2]),
+    (2, 96, 200, [200, 150]),
+    (1, 256, 130, [130]),
+    (2, 128, 40, [5, 40]),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}_H{c[1]}_T{c[2]}")
+@pytest.mark.parametrize("P", [0, 32, 100, 4096])
+def test_mla_matches_oracle(gpu, case, P):
+    m = _m()
+    B, H, T, lens = case
+    w = W.small_mla(B, H, T, seed=21)
+    (qn, qr, lat, l), (gqn, gqr, glat, gl) = _inputs(w, gpu, lens)
+    ref = oracle.decode_mla(qn, qr, lat, l, w.scale, w.d_c)
+    if P == 0:
+        got = _f64(m.attn_decode_mla(gqn, gqr, glat, gl, w.scale))
+        assert np.all(np.abs(got - ref) <= 2e-3 + _half_ulp_bf16(ref)), float(np.abs(got - ref).max())
+    else:
+        got = _f64(_fp32_out(m, gqn, gqr, glat, gl, w.scale, P))
+        err = float(np.abs(got - ref).max())
+        assert err <= 2e-3, err
+
+
+def test_peaked_scores_short_rows(gpu):
+    """Few positions with large score gaps: the case where rounding the weights
+    to bf16 alone would exceed 2e-3; the hi/lo weight split keeps it far below."""
+    m = _m()
+    w = W.small_mla(4, 128, 64, seed=22)
+    (qn, qr, lat, l), (gqn, gqr, glat, gl) = _inputs(w, gpu, [2, 3, 5, 64])
+    qn3, qr3 = qn * 3, qr * 3                      # sharper softmax
+    ref = oracle.decode_mla(qn3, qr3, lat, l, w.scale, w.d_c)
+    got = _f64(_fp32_out(m, qn3.to(gpu), qr3.to(gpu), glat, gl, w.scale, 32))
+    err = float(np.abs(got - ref).max())
+    assert err <= 2e-4, err
+
+
+def test_single_position_is_bit_exact(gpu):
+    m = _m()
+    w = W.small_mla(3, 128, 100, seed=23)
+    _, (gqn, gqr, glat, gl) = _inputs(w, gpu, [1, 1, 1])
+    out = m.attn_decode_mla(gqn, gqr, glat, gl, w.scale)
+    expect = glat[:, 0, :512].unsqueeze(1).expand(3, 128, 512)
+    assert torch.equal(out, expect)
+
+
+def test_zero_length_rows(gpu):
+    m = _m()
+    w = W.small_mla(3, 64, 100, seed=24)
+    (qn, qr, lat, l), (gqn, gqr, glat, gl) = _inputs(w, gpu, [0, 77, -5])
+    out = m.attn_decode_mla(gqn, gqr, glat, gl, w.scale)
+    assert torch.equal(out[0], torch.zeros_like(out[0]))
+    assert torch.equal(out[2], torch.zeros_like(out[2]))
+    ref = oracle.decode_mla(qn, qr, lat, l, w.scale, w.d_c)
+    assert np.all(np.abs(_f64(out) - ref) <= 2e-3 + _half_ulp_bf16(ref))
+
+
+def test_nan_padding_is_never_read(gpu):
+    m = _m()
+    w = W.small_mla(2, 128, 512, seed=25)
+    _, (gqn, gqr, glat, gl) = _inputs(w, gpu, [300, 33])
+    base = m.attn_decode_mla(gqn, gqr, glat, gl, w.scale)
+    g2 = glat.clone()
+    g2[0, 300:] = float("nan")
+    g2[1, 33:] = float("inf")
+    out = m.attn_decode_mla(gqn, gqr, g2, gl, w.scale)
+    assert torch.equal(out, base) and torch.isfinite(out).all()
+
+
+def test_deterministic_and_partition_invariant(gpu):
+    m = _m()
+    w = W.small_mla(4, 128, 2048, seed=26, lens=(1, 2048))
+    (qn, qr, lat, l), (gqn, gqr, glat, gl) = _inputs(w, gpu)
+    a = m.attn_decode_mla(gqn, gqr, glat, gl, w.scale)
+    b = m.attn_decode_mla(gqn, gqr, glat, gl, w.scale)
+    assert torch.equal(a, b)
+    one = _f64(_fp32_out(m, gqn, gqr, glat, gl, w.scale, 2048))
+    many = _f64(_fp32_out(m, gqn, gqr, glat, gl, w.scale, 96))
+    assert float(np.abs(one - many).max()) <= 1e-5
+
+
+def test_partials_match_oracle_per_partition(gpu):
+    m = _m()
+    w = W.small_mla(1, 128, 300, seed=27)
+    (qn, qr, lat, l), (gqn, gqr, glat, gl) = _inputs(w, gpu, [300])
+    P = 128
+    po, pl = m.attn_decode_mla_partial(gqn, gqr, glat, gl, w.scale, P)
+    po, pl = _f64(po), _f64(pl)
+    q = torch.cat([qn, qr], dim=-1)
+    for p in range(3):
+        lo, hi = p * P, min(p * P + P, 300)
+        ref = oracle.decode_mla(qn, qr, lat[:, lo:hi], [hi - lo], w.scale, w.d_c)
+        assert float(np.abs(po[:, :, p] - ref).max()) <= 2e-3
+        lse = oracle.decode_gqa_lse(q, lat[:, None, lo:hi], [hi - lo], w.scale) / math.log(2)
+        assert float(np.abs(pl[:, :, p] - lse).max()) <= 1e-4
+
+
+def test_full_size_workload_sampled_rows(gpu):
+    """DeepSeek-V2-shaped layer (B=64, H=128, T=4096) in the benchmark's launch
+    configuration; the oracle checks every head of a sample of sequences."""
+    m = _m()
+    w = W.MLA_V2
+    (qn, qr, lat, l), (gqn, gqr, glat, gl) = _inputs(w, gpu)
+    got = _f64(m.attn_decode_mla(gqn, gqr, glat, gl, w.scale))
+    assert np.isfinite(got).all()
+    worst = 0.0
+    for b in (0, 17, 40, 63):
+        ref = oracle.decode_mla(qn[b:b + 1], qr[b:b + 1], lat[b:b + 1], l[b:b + 1], w.scale, w.d_c)[0]
+        worst = max(worst, float(np.abs(got[b] - ref).max()))
+        assert np.all(np.abs(got[b] - ref) <= 2e-3 + _half_ulp_bf16(ref))
+    print(f"mla full size: worst sampled max-abs error {worst:.3e}")
+    assert worst <= 2e-3

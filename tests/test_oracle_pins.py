@@ -344,3 +344,22 @@ def test_mla_rotary_part_enters_the_score_only():
     c = oracle.decode_mla(qn, qr, lat2, [T], 0.5, d_c)
     d = oracle.decode_mla(qn, torch.zeros_like(qr), lat, [T], 0.5, d_c)
     assert np.array_equal(c, d)                             # with no rotary score, keys are the latent alone
+
+
+# --------------------------------------------------------------------------- log-sum-exp
+
+def test_lse_closed_form_and_brute():
+    # scores ln 2 and ln 3 (one key dimension, q = 1, scale 1): log(2 + 3)
+    k = torch.tensor([[[[math.log(2.0)], [math.log(3.0)], [99.0]]]], dtype=torch.float64)
+    q = torch.ones(1, 1, 1, dtype=torch.float64)
+    assert abs(oracle.decode_gqa_lse(q, k, [2], 1.0)[0, 0] - math.log(5.0)) <= 1e-15
+    assert oracle.decode_gqa_lse(q, k, [0], 1.0)[0, 0] == -np.inf
+    # against scalar loops with math.fsum, and the weights recovered from it sum to one
+    qq, kk = _rand((2, 6, 5), 92), _rand((2, 3, 9, 5), 93)
+    lse = oracle.decode_gqa_lse(qq, kk, [9, 4], 0.6)
+    for b, n in enumerate([9, 4]):
+        for i in range(6):
+            s = [0.6 * math.fsum(x * y for x, y in zip(qq[b, i].tolist(), kk[b, i // 2, t].tolist()))
+                 for t in range(n)]
+            assert abs(lse[b, i] - math.log(math.fsum(math.exp(x) for x in s))) <= 1e-12
+            assert abs(math.fsum(math.exp(x - lse[b, i]) for x in s) - 1.0) <= 1e-14

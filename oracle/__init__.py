@@ -30,6 +30,7 @@ from .attention import (  # noqa: F401
     decode_gqa,
     decode_mla,
     decode_gqa_weights,
+    decode_gqa_lse,
     clamp_len,
 )
 from .cache import kv_cache_bytes, mla_cache_bytes  # noqa: F401

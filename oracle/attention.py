@@ -127,6 +127,29 @@ def decode_gqa_weights(q, k_cache, seq_lens, scale: float) -> list:
     return res
 
 
+def decode_gqa_lse(q, k_cache, seq_lens, scale: float) -> np.ndarray:
+    """Natural log of sum_t exp(s_t) per row, s_t the scaled scores of ``decode_gqa``.
+
+    float64 [B, h_q]; rows with n == 0 hold -inf (an empty sum). This is the
+    normaliser of the softmax, the quantity by which split partial results
+    are weighted when they are combined.
+    """
+    B, h_q, D = q.shape
+    _, h_kv, T_max, _ = k_cache.shape
+    g = h_q // h_kv
+    lens = _lens(seq_lens, B)
+    res = np.full((B, h_q), -np.inf)
+    for b in range(B):
+        n = clamp_len(lens[b], T_max)
+        if n == 0:
+            continue
+        for j in range(h_kv):
+            S = scale * (_f64(q[b, j * g:(j + 1) * g]) @ _f64(k_cache[b, j, :n]).T)
+            m = S.max(axis=1)
+            res[b, j * g:(j + 1) * g] = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
+    return res
+
+
 def decode_mla(q_nope, q_rope, latent, seq_lens, scale: float, d_c: int) -> np.ndarray:
     """Absorbed multi-head latent attention, one decode step.
 

@@ -176,7 +176,8 @@ def main():
 
             def merge(po=po, pl=pl, gl=gl, P=P, out=out, w=w):
                 m.attn_decode_merge(po, pl, gl, w.T_max, P, out=out)
-            kname = f"gqa_partial_kernel<BF16Elem, {w.D}, {w.group}>"
+            kname = (f"gqa_partial_po_kernel<{w.D}, {w.group}>" if w.group <= 8
+                     else f"gqa_partial_kernel<BF16Elem, {w.D}, {w.group}>")
             src = os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "gqa_decode.hip")
         else:
             qn, qr, lat, gl = gpu

@@ -56,13 +56,14 @@ int check_gqa_shape(const GqaShape& s) {
   return ATTN_OK;
 }
 
-// Positions per partition: a power of two in [256, 4096] chosen so that the
-// (b, kv head, partition) grid holds about 2048 work-groups (8 per CU on the
-// 256-CU part) when the cache is full.
+// Positions per partition: a power of two in [512, 4096] chosen so that the
+// (b, kv head, partition) grid holds about 8192 work-groups (32 per CU on the
+// 256-CU part) when the cache is full. A work-group's 4 waves take 64-position
+// tiles in turn, so 512 positions give each wave two tiles.
 int gqa_auto_partition(const GqaShape& s) {
   const int64_t pairs = int64_t(s.B) * s.h_kv;
-  const int64_t want = (int64_t(s.T_max) * pairs + 2047) / 2048;
-  int P = 256;
+  const int64_t want = (int64_t(s.T_max) * pairs + 8191) / 8192;
+  int P = 512;
   while (P < want && P < 4096) P <<= 1;
   return P;
 }

@@ -53,4 +53,70 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Value held by lane l ^ 16 (v_permlane16_swap) and by lane l ^ 32
+// (v_permlane32_swap). Each swap leaves a lane with its own value and its
+// partner's, in an order that depends on the lane's half; max and sum do not
+// care about the order.
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Maximum / sum over all 64 lanes; every lane ends with the result.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_mov<kDppXor1>(x));
+  x = fmaxf(x, dpp_mov<kDppXor2>(x));
+  x = fmaxf(x, dpp_mov<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp_mov<kDppMirror>(x));
+  return xor32_max(xor16_max(x));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_mov<kDppXor1>(x);
+  x += dpp_mov<kDppXor2>(x);
+  x += dpp_mov<kDppHalfMirror>(x);
+  x += dpp_mov<kDppMirror>(x);
+  return xor32_sum(xor16_sum(x));
+}
+
+// Issue one 16-byte-per-lane copy from global memory straight into LDS
+// (global_load_lds_dwordx4): lane i's 16 bytes land at lds_base + 16*i.
+// lds_base must be wave-uniform. Written as inline assembly so that the
+// compiler does not wait for the copy before unrelated LDS reads; the caller
+// waits with s_waitcnt vmcnt. The instruction writes no register, only LDS;
+// M0 carries the LDS address and no other code in these kernels uses M0.
+__device__ __forceinline__ void copy16_to_lds(uint32_t lds_base, const void* src) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(src) : "memory");
+}
+
+// Same copy with a wave-uniform base address (scalar register pair) and a
+// per-lane 32-bit byte offset: one VGPR per lane instead of a 64-bit address.
+__device__ __forceinline__ void copy16_to_lds_sbase(uint32_t lds_base, const void* sbase, uint32_t voff) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  // readfirstlane returns a signed int: widen each half through uint32_t so
+  // the low half is zero-extended (a sign-extended low half would corrupt the
+  // upper 32 address bits whenever its bit 31 is set).
+  const uint64_t sb = (uint64_t)(uintptr_t)sbase;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32));
+  const uint64_t sbu = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(base), "v"(voff), "s"(sbu) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)p;
+}
+
 }  // namespace attn

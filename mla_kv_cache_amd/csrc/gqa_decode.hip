@@ -221,6 +221,242 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel, one cached position per lane for the scores.
+//
+// Each wave owns tiles of 64 positions (tiles are dealt to the 4 waves in
+// turn). For a tile:
+//  * K rows go straight from HBM into the wave's own LDS area (direct copy,
+//    16 bytes per lane per instruction). Within each row the 16-byte chunks
+//    are stored XOR-permuted by the row index, so that 16 lanes reading the
+//    same logical chunk of 16 different rows hit 16 different bank groups.
+//  * Lane t scores position t0 + t against all G query heads: the query is
+//    the same for every lane, so the compiler keeps it in scalar registers
+//    and each v_dot2 takes it as its scalar operand; no cross-lane reduction.
+//  * The tile maximum per head is one wave-wide reduction; the running
+//    maximum is wave-uniform. Each weight exp2(s - m) is computed once, by
+//    the lane that owns the position, and written to a small LDS table.
+//  * V rows are loaded into registers in the row layout (LPR lanes x 16 bytes
+//    per row, 1 KiB contiguous per wave-wide load), and each lane reads the G
+//    weights of its row from the table (a broadcast read) for the product.
+// Compared with reducing every score across a row's lanes, the arithmetic per
+// cached element drops from G*(2 + 4/8) lane-ops + G exps per row group to
+// about G/2 dot2 + G/64 exps, which is what matters when G = 4..8.
+constexpr int kPoRows = 64;
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ seq_lens, int h_kv, int T_max,
+    int P, int NP, float qk_scale_log2, float* __restrict__ part_out,
+    float* __restrict__ part_lse) {
+  constexpr int CH = D / 8;              // 16-byte chunks per row
+  constexpr int LPR = CH;                // lanes per row in the V layout
+  constexpr int RPI = 64 / LPR;          // rows per wave-wide V load
+  constexpr int NV = kPoRows / RPI;      // V loads per tile
+  constexpr int KBYTES = kPoRows * D * 2;
+  constexpr int NK = KBYTES / 1024;      // K copies per tile (one KiB each)
+  constexpr int GP = (G + 3) / 4 * 4;   // weight-table row, padded to whole float4s
+  static_assert(NV <= 32 && NK <= 32, "tile too large");
+
+  __shared__ __attribute__((aligned(1024))) unsigned char ktile[kWaves][KBYTES];
+  __shared__ __attribute__((aligned(16))) float wtab[kWaves][kPoRows][GP];
+
+  const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int n = min(max(seq_lens[b], 0), T_max);
+  const int start = p * P;
+  if (start >= n) return;
+  const int end = min(start, n - P) + P;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rr = lane / LPR, c = lane % LPR;
+  const int H = h_kv * G;
+
+  // Query of the G heads, read with uniform addresses (scalar loads).
+  const uint32_t* qw = reinterpret_cast<const uint32_t*>(q + ((size_t)b * H + (size_t)j * G) * D);
+
+  float m[G], lpart[G], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kNegInf;
+    lpart[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+
+  const size_t head_off = ((size_t)b * h_kv + j) * (size_t)T_max * D;
+  const uint16_t* kb = kc + head_off;
+  const uint16_t* vb = vc + head_off + (size_t)c * 8;
+  const uint32_t kt_lds = lds_addr(&ktile[wave][0]);
+  const unsigned char* kt = &ktile[wave][0];
+  float* wt = &wtab[wave][0][0];
+
+  // K tile -> LDS (slot = 64*i + lane holds row slot/CH, stored chunk slot%CH,
+  // which carries logical chunk (slot%CH) ^ (row % CH)).
+  auto copy_k = [&](int t0) {
+    const uint16_t* tbase = kb + (size_t)t0 * D;  // wave-uniform
+    // Partly unrolled on purpose: fully unrolled, the per-slot offsets are
+    // loop-invariant and get hoisted out of the tile loop, costing registers.
+#pragma unroll 4
+    for (int i = 0; i < NK; ++i) {
+      const int slot = 64 * i + lane;
+      const int r = slot / CH, pc = slot % CH;
+      const int lc = pc ^ (r % CH);
+      const int rr_ = min(t0 + r, end - 1) - t0;
+      copy16_to_lds_sbase(kt_lds + 1024u * i, tbase, (uint32_t)(rr_ * D + lc * 8) * 2u);
+    }
+  };
+  // V rows -> registers (row layout), one wave-wide load per RPI rows.
+  auto load_v = [&](int t0, int i) { return ld16(vb + (size_t)min(t0 + i * RPI + rr, end - 1) * D); };
+
+  for (int t0 = start + wave * kPoRows; t0 < end; t0 += kWaves * kPoRows) {
+    copy_k(t0);
+    uint4 vr[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) vr[i] = load_v(t0, i);
+    // The K copies were issued first: once at most NV memory operations of
+    // this wave are outstanding, they have all landed.
+    if constexpr (NV == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if constexpr (NV == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // ---- scores: lane owns position t0 + lane; its K row comes out of LDS
+    // in one batch, then G dot products run on it.
+    const unsigned char* krow = kt + lane * (D * 2);
+    uint4 kk[CH];
+#pragma unroll
+    for (int jc = 0; jc < CH; ++jc) kk[jc] = *reinterpret_cast<const uint4*>(krow + 16 * (jc ^ (lane % CH)));
+    float s[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) s[h] = 0.f;
+#pragma unroll
+    for (int jc = 0; jc < CH; ++jc) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const uint32_t* qh = qw + h * (D / 2) + 4 * jc;
+        float a = s[h];
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[0]), __builtin_bit_cast(bf16x2, kk[jc].x), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[1]), __builtin_bit_cast(bf16x2, kk[jc].y), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[2]), __builtin_bit_cast(bf16x2, kk[jc].z), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[3]), __builtin_bit_cast(bf16x2, kk[jc].w), a, false);
+        s[h] = a;
+      }
+    }
+    // The K area is rewritten by the next tile's copy: all its reads are done.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const bool valid = t0 + lane < end;
+    bool need = false;
+    float mx[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s[h] = valid ? s[h] * qk_scale_log2 : kNegInf;
+      mx[h] = wave_max(s[h]);
+      need |= mx[h] > m[h] + kTau;
+    }
+    if (need) {  // wave-uniform: the maxima are wave-wide
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const bool nh = mx[h] > m[h] + kTau;
+        const float f = nh ? fast_exp2(m[h] - mx[h]) : 1.f;
+        m[h] = nh ? mx[h] : m[h];
+        lpart[h] *= f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= f;
+      }
+    }
+    float w[GP];
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      w[h] = (h < G && valid) ? fast_exp2(s[h < G ? h : 0] - m[h < G ? h : 0]) : 0.f;
+      if (h < G) lpart[h] += w[h];
+    }
+#pragma unroll
+    for (int h = 0; h < GP; h += 4)
+      *reinterpret_cast<float4*>(wt + lane * GP + h) = make_float4(w[h], w[h + 1], w[h + 2], w[h + 3]);
+
+    // ---- output: lane (rr, c) accumulates rows i*RPI + rr, dims 8c .. 8c+7
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const float* wr = wt + (i * RPI + rr) * GP;
+      float wv[GP];
+#pragma unroll
+      for (int h = 0; h < GP; h += 4) {
+        const float4 t = *reinterpret_cast<const float4*>(wr + h);
+        wv[h] = t.x;
+        wv[h + 1] = t.y;
+        wv[h + 2] = t.z;
+        wv[h + 3] = t.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t wd = word(vr[i], e >> 1);
+        const float x = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h][e] = fmaf(wv[h], x, acc[h][e]);
+      }
+    }
+  }
+
+  // All lanes of a wave share m: the row groups add up, the per-position sums add up.
+  float L[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    L[h] = wave_sum(lpart[h]);
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, 64);
+  }
+
+  // Combine the waves through LDS and write this partition's partial. The
+  // per-wave sums reuse the K tile area once every wave has left its loop.
+  static_assert(sizeof(float) * kWaves * G * D <= sizeof(ktile), "combine area too small");
+  __shared__ float sm_m[kWaves][G];
+  __shared__ float sm_l[kWaves][G];
+  __syncthreads();
+  float (*sm_acc)[G][D] = reinterpret_cast<float (*)[G][D]>(&ktile[0][0]);
+  if (lane < LPR) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm_acc[wave][h][c * 8 + e] = acc[h][e];
+      if (c == 0) {
+        sm_m[wave][h] = m[h];
+        sm_l[wave][h] = L[h];
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int h = idx / D, d = idx % D;
+    float M = sm_m[0][h];
+#pragma unroll
+    for (int w2 = 1; w2 < kWaves; ++w2) M = fmaxf(M, sm_m[w2][h]);
+    float Ls = 0.f, A = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) {
+      const float mw = sm_m[w2][h];
+      const float f = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
+      Ls += sm_l[w2][h] * f;
+      A += sm_acc[w2][h][d] * f;
+    }
+    const size_t row = ((size_t)b * H + (size_t)j * G + h) * NP + p;
+    part_out[row * D + d] = A / Ls;
+    if (d == 0) part_lse[row] = M + fast_log2(Ls);
+  }
+}
+
+template <int D, int G>
+hipError_t launch_po(const void* q, const void* k, const void* v, const int32_t* lens, int B,
+                     int h_kv, int T_max, int P, int NP, float sc, float* po, float* pl,
+                     hipStream_t stream) {
+  dim3 grid(NP, h_kv, B);
+  hipLaunchKernelGGL((gqa_partial_po_kernel<D, G>), grid, dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), lens, h_kv, T_max, P, NP, sc, po, pl);
+  return hipGetLastError();
+}
+
 template <class E, int D, int G>
 hipError_t launch_one(const void* q, const void* k, const void* v, const int32_t* lens, int B,
                       int h_kv, int T_max, int P, int NP, float sc, float* po, float* pl,
@@ -233,10 +469,27 @@ hipError_t launch_one(const void* q, const void* k, const void* v, const int32_t
   return hipGetLastError();
 }
 
+#ifndef ATTN_PO_MIN_GROUP
+#define ATTN_PO_MIN_GROUP 1
+#endif
+// Smallest group size served by the position-per-lane kernel (bf16 only).
+constexpr int kPoMinGroup = ATTN_PO_MIN_GROUP;
+
 template <class E, int D>
 hipError_t launch_d(int G, const void* q, const void* k, const void* v, const int32_t* lens, int B,
                     int h_kv, int T_max, int P, int NP, float sc, float* po, float* pl,
                     hipStream_t s) {
+  if constexpr (sizeof(typename E::storage) == 2) {
+    if (G >= kPoMinGroup) {
+      switch (G) {
+        case 1: return launch_po<D, 1>(q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
+        case 2: return launch_po<D, 2>(q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
+        case 4: return launch_po<D, 4>(q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
+        case 8: return launch_po<D, 8>(q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
+        default: break;
+      }
+    }
+  }
   switch (G) {
     case 1: return launch_one<E, D, 1>(q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
     case 2: return launch_one<E, D, 2>(q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);

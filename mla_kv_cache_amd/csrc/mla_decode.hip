@@ -64,19 +64,37 @@ constexpr int kTile = 32;                  // positions per tile
 constexpr int kStride = kRow + 8;          // LDS row stride in bf16 (1168 bytes)
 constexpr int kSteps = kRow / 16;          // 36 k-steps of the score product
 constexpr int kOTiles = kDc / 32;          // 16 output tiles of 32 latent dims
-constexpr int kChunks = kTile * kRow / 8;  // 16-byte chunks per tile (2304)
 constexpr float kTau = 8.0f;
 
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
-__device__ __forceinline__ float bf16_round(float a) {
-  return __uint_as_float((uint32_t)f32_to_bf16_rne(a) << 16);
+
+// The value held by lane l ^ 32 (v_permlane32_swap exchanges the two halves of
+// the wave; each lane ends with its own value and its partner's).
+__device__ __forceinline__ float partner_half(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return (threadIdx.x & 32) ? a : b;
 }
 
 constexpr int kRowChunks = kStride / 8;               // 73 16-byte chunks per LDS row (72 + pad)
-constexpr int kBufBytes = (kTile * kStride * 2 + 1023) / 1024 * 1024;  // 37888: whole 1 KiB copy blocks
-constexpr int kBlocks = kBufBytes / 1024;                // 37 wave-wide copies per tile
+constexpr int kTileBlocks = (kTile * kStride * 2 + 1023) / 1024;  // 37 1 KiB blocks hold a tile
+
+// Copy blocks per tile for a work-group of NWAVES waves: rounded up so every
+// wave issues the same number of copies (the extra blocks land in slack space
+// at the end of the buffer); the per-wave count is what s_waitcnt vmcnt waits on.
+template <int NWAVES>
+struct TileCopy {
+  static constexpr int kPerWave = (kTileBlocks + NWAVES - 1) / NWAVES;
+  static constexpr int kBlocks = kPerWave * NWAVES;
+  static constexpr int kBufBytes = kBlocks * 1024;
+};
 constexpr int kHalfSteps = kSteps / 2;                   // 18 score k-steps per wave
 constexpr int kHalfTiles = kOTiles / 2;                  // 8 output tiles per wave
 
@@ -95,7 +113,9 @@ template <int NWAVES>
 __device__ __forceinline__ void copy_tile(unsigned char* buf, const uint16_t* lat_b, int t0, int end,
                                           int wave, int lane) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)buf;
-  for (int blk = wave; blk < kBlocks; blk += NWAVES) {
+#pragma unroll
+  for (int k = 0; k < TileCopy<NWAVES>::kPerWave; ++k) {
+    const int blk = wave + NWAVES * k;
     const int ci = 64 * blk + lane;
     const int row = ci / kRowChunks, c16 = ci % kRowChunks;
     const bool data = row < kTile && c16 < kRow / 8;
@@ -106,6 +126,23 @@ __device__ __forceinline__ void copy_tile(unsigned char* buf, const uint16_t* la
   }
 }
 
+// Wait until this wave's copies of the current tile have landed while the
+// copies of the next tile (kPerWave of them, issued later) may still be in
+// flight, then barrier: afterwards every wave's copies of the current tile
+// are in LDS and every wave is done with the tile before it.
+template <int N>
+__device__ __forceinline__ void wait_tile_barrier(bool next_in_flight) {
+  if (next_in_flight) {
+    if constexpr (N == 19) asm volatile("s_waitcnt vmcnt(19) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (N == 7) asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else static_assert(N == 5, "no wait defined for this copy count");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+}
+
 template <int NHB>
 __global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
@@ -113,10 +150,13 @@ __global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(
     int P, int NP, float qk_scale_log2, float* __restrict__ part_out,
     float* __restrict__ part_lse) {
   constexpr int NWAVES = 2 * NHB;
-  // Two tile buffers as separate objects: the compiler can then tell the copy
-  // into one from the reads of the other and does not wait for the copy.
-  __shared__ __attribute__((aligned(1024))) unsigned char buf0[kBufBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char buf1[kBufBytes];
+  // Three tile buffers as separate objects: the copies of the next two tiles
+  // are in flight while one is computed, and the compiler can tell the copy
+  // into one buffer from the reads of another.
+  using TC = TileCopy<NWAVES>;
+  __shared__ __attribute__((aligned(1024))) unsigned char buf0[TC::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf1[TC::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf2[TC::kBufBytes];
   __shared__ __attribute__((aligned(16))) unsigned char xbuf[NWAVES * 4096];
 
   const int p = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;
@@ -156,14 +196,12 @@ __global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(
   const int tr_row = 4 * (g16 >> 1) + (i16 >> 2);
   const int tr_col = 256 * kh + 16 * (g16 & 1) + 4 * (i16 & 3);
 
-  // One tile: wait for its copy, start the next copy into the other buffer,
-  // then scores, exchange, softmax and the output product.
+  // One tile: wait for its copy, start the copy of the tile after next into
+  // the third buffer, then scores, exchange, softmax and the output product.
   auto tile = [&](const unsigned char* __restrict__ cur_b, unsigned char* __restrict__ nxt_b, int t0) {
     const uint16_t* cur = reinterpret_cast<const uint16_t*>(cur_b);
-    // This wave's copies of this tile have landed; after the barrier everyone's
-    // have, and every wave is done with the other buffer.
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (t0 + kTile < end) copy_tile<NWAVES>(nxt_b, lat_b, t0 + kTile, end, wave, lane);
+    wait_tile_barrier<TC::kPerWave>(t0 + kTile < end);
+    if (t0 + 2 * kTile < end) copy_tile<NWAVES>(nxt_b, lat_b, t0 + 2 * kTile, end, wave, lane);
 
     // ---- partial scores over this wave's 288 dims: S^T = L . Q^T
     f32x16 s;
@@ -197,13 +235,23 @@ __global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(
     // ---- online softmax for head `col` over this tile's positions
     float x[16];
     float mt = kNegInf;
+    if (t0 + kTile <= end) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int pos = t0 + 8 * (r >> 2) + 4 * half + (r & 3);
-      x[r] = pos < end ? s[r] * qk_scale_log2 : kNegInf;
-      mt = fmaxf(mt, x[r]);
+      for (int r = 0; r < 16; ++r) {
+        x[r] = s[r] * qk_scale_log2;
+        mt = fmaxf(mt, x[r]);
+      }
+    } else {  // the last tile of the partition: positions past `end` get no weight
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int pos = t0 + 8 * (r >> 2) + 4 * half + (r & 3);
+        x[r] = pos < end ? s[r] * qk_scale_log2 : kNegInf;
+        mt = fmaxf(mt, x[r]);
+      }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = fmaxf(mt, partner_half(mt));
+    // The first tile always sets m (its first position is valid), so m is finite
+    // below and exp2(x - m) is 0 for masked positions without a select.
     const bool need = mt > m + kTau;
     if (__any(need)) {
       const float f = need ? fast_exp2(m - mt) : 1.f;
@@ -217,26 +265,21 @@ __global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(
     // Weights as a bf16 pair hi + lo (hi = bf16(p), lo = bf16(p - hi)): the
     // product below runs once per part on the same latent fragment, so the
     // weights enter with ~2^-17 relative error instead of bf16's 2^-9.
-    float pr[16];
+    uint32_t ph[8], pl[8];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      pr[r] = x[r] == kNegInf ? 0.f : fast_exp2(x[r] - m);
-      lsum += pr[r];
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = fast_exp2(x[r] - m), p1 = fast_exp2(x[r + 1] - m);
+      lsum += p0 + p1;
+      const uint32_t h = pack_bf16x2(p0, p1);
+      ph[r >> 1] = h;
+      pl[r >> 1] = pack_bf16x2(p0 - bf16_lo(h), p1 - bf16_hi(h));
     }
 
     // ---- O^T += L^T . P^T over this wave's 256 output dims (two k-steps of 16 positions)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      uint32_t ph[4], pl[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = pr[8 * ks + 2 * e], p1 = pr[8 * ks + 2 * e + 1];
-        const float h0 = bf16_round(p0), h1 = bf16_round(p1);
-        ph[e] = pack_bf16(h0, h1);
-        pl[e] = pack_bf16(p0 - h0, p1 - h1);
-      }
-      const bf16x8 pbh = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
-      const bf16x8 pbl = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+      const bf16x8 pbh = __builtin_bit_cast(bf16x8, make_uint4(ph[4 * ks], ph[4 * ks + 1], ph[4 * ks + 2], ph[4 * ks + 3]));
+      const bf16x8 pbl = __builtin_bit_cast(bf16x8, make_uint4(pl[4 * ks], pl[4 * ks + 1], pl[4 * ks + 2], pl[4 * ks + 3]));
       const uint16_t* base = cur + (16 * ks + tr_row) * kStride + tr_col;
 #pragma unroll
       for (int t = 0; t < kHalfTiles; ++t) {
@@ -255,15 +298,18 @@ __global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(
   };
 
   copy_tile<NWAVES>(buf0, lat_b, start, end, wave, lane);
+  if (start + kTile < end) copy_tile<NWAVES>(buf1, lat_b, start + kTile, end, wave, lane);
   for (int t0 = start;;) {
-    tile(buf0, buf1, t0);
+    tile(buf0, buf2, t0);
     if ((t0 += kTile) >= end) break;
     tile(buf1, buf0, t0);
+    if ((t0 += kTile) >= end) break;
+    tile(buf2, buf1, t0);
     if ((t0 += kTile) >= end) break;
   }
 
   // Lanes l and l^32 share a head and a running maximum; add their sums.
-  lsum += __shfl_xor(lsum, 32, 64);
+  lsum += partner_half(lsum);
   const float inv = 1.f / lsum;
   const size_t prow = ((size_t)b * H + head) * NP + p;
   float* po = part_out + prow * kDc + 256 * kh;

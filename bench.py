@@ -75,10 +75,90 @@ def traffic_for(kernel_src: str, kernel_name: str):
     except Exception:
         return None
     sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
-    ent = rec.get(kernel_name)
+    ent = rec.get("kernels", {}).get(kernel_name)
     if not ent or ent.get("source_sha256") != sha:
         return None
     return ent.get("hbm_bytes_per_launch")
+
+
+COPY_CAL_BYTES = 1 << 30   # size of the plain device-to-device copy used to calibrate counters
+COPY_CAL_REPS = 4
+
+
+def copy_calibration(dev):
+    """Plain device-to-device copies of a known size (read COPY_CAL_BYTES, write COPY_CAL_BYTES).
+
+    Run after the timed region when --copy-calibration is given, so that a
+    rocprofv3 counter run over the same command can scale FETCH_SIZE and
+    WRITE_SIZE to bytes."""
+    import torch
+    a = torch.ones(COPY_CAL_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(COPY_CAL_REPS):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def _norm_kernel_name(full: str) -> str:
+    s = full.replace("attn::(anonymous namespace)::", "")
+    if s.startswith("void "):
+        s = s[5:]
+    return s.split("(")[0].strip()
+
+
+def _read_counter(path: str, counter: str):
+    """[(dispatch_id, kernel_name, value)] for one counter from a rocprofv3 counter_collection CSV."""
+    import csv
+    out = []
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            out.append((int(row["Dispatch_Id"]), _norm_kernel_name(row["Kernel_Name"]),
+                        float(row["Counter_Value"])))
+    return out
+
+
+def write_traffic(fetch_csv: str, write_csv: str, command: str):
+    """Turn two rocprofv3 --pmc runs of ``bench.py --copy-calibration`` (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch) into profiles/traffic.json.
+
+    The calibration copies are the copy-kernel dispatches issued after the last
+    attention kernel; each moves COPY_CAL_BYTES in and out, so
+    factor = COPY_CAL_BYTES / (counter KiB * 1024) converts a counter reading to bytes."""
+    srcs = {"gqa_partial": os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "gqa_decode.hip"),
+            "mla_partial": os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "mla_decode.hip"),
+            "lse_merge": os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "lse_merge.hip")}
+    res = {"command": command, "copy_bytes": COPY_CAL_BYTES, "kernels": {}}
+    per = {}
+    for cname, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _read_counter(path, cname)
+        attn = [r for r in rows if any(r[1].startswith(k) for k in srcs)]
+        last = max(r[0] for r in attn)
+        cal = [r[2] for r in rows if r[0] > last and "copyBuffer" in r[1]]
+        if not cal:
+            raise SystemExit(f"{path}: no calibration copy dispatches after the attention kernels")
+        kib = sum(cal) / len(cal)
+        factor = COPY_CAL_BYTES / (kib * 1024.0)
+        res[cname] = {"copy_kib_per_dispatch": kib, "factor": factor, "copy_dispatches": len(cal)}
+        for _, name, v in attn:
+            per.setdefault(name, {}).setdefault(cname, []).append(v * 1024.0 * factor)
+    for name, d in sorted(per.items()):
+        src = next(p for k, p in srcs.items() if name.startswith(k))
+        fb = sum(d["FETCH_SIZE"]) / len(d["FETCH_SIZE"])
+        wb = sum(d["WRITE_SIZE"]) / len(d["WRITE_SIZE"])
+        res["kernels"][name] = {
+            "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+            "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+            "hbm_bytes_per_launch": round(fb + wb), "launches": len(d["FETCH_SIZE"])}
+    out = os.path.join(ROOT, "profiles", "traffic.json")
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res, indent=1))
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -125,7 +205,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--skip-mha", action="store_true", help="do not time the MHA breakdown workload")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run plain 1 GiB device copies (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 counter CSVs and exit")
+    ap.add_argument("--traffic-command", default="", help="command recorded with --traffic-from")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        write_traffic(args.traffic_from[0], args.traffic_from[1], args.traffic_command)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library runs on a single MI355X and has no "
@@ -192,7 +281,7 @@ def main():
 
             def merge(po=po, pl=pl, gl=gl, P=P, out=out, w=w):
                 m.attn_decode_merge(po, pl, gl, w.T_max, P, out=out)
-            kname = "mla_partial_kernel"
+            kname = f"mla_partial_kernel<{4 if w.H >= 128 else w.H // 32}>"
             src = os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "mla_decode.hip")
         items.append(dict(name=name, kind=kind, w=w, partial=partial, merge=merge, kv=kv,
                           other=other, flops=flops, P=P, NP=NP, kname=kname, src=src,
@@ -302,6 +391,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cpu_items, args.cpu_budget)
+    if args.copy_calibration:
+        copy_calibration(dev)
     print(json.dumps(res), flush=True)
 
 

@@ -101,7 +101,9 @@ uint64_t attn_mla_cache_bytes(uint64_t n_layers, uint64_t d_c, uint64_t d_r,
  * seq_lens int32 [B]
  * out      [B, h_q, D]           dtype dt
  * Supported: D in {64, 128}; g = h_q / h_kv in {1, 2, 4, 8, 16}; dt in
- * {ATTN_F32, ATTN_BF16}. Any B >= 1, T_max >= 1 with B*h_kv*T_max*D < 2^40.
+ * {ATTN_F32, ATTN_BF16}. Any B >= 1, T_max >= 1 with B*h_kv*T_max*D < 2^40;
+ * one (sequence, KV head) slab, T_max*D*sizeof(elem), must stay below 2 GiB
+ * (ATTN_ERR_UNSUPPORTED otherwise).
  */
 
 /* The library's plan for a shape: partition size (positions per split),

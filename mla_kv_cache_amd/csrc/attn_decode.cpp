@@ -53,6 +53,8 @@ int check_gqa_shape(const GqaShape& s) {
   if (int64_t(s.B) * s.h_q >= (int64_t(1) << 31)) return ATTN_ERR_INVALID_ARG;
   if (s.dt != ATTN_F32 && s.dt != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (!attn::gqa_supported(int(s.dt), s.D, s.h_q / s.h_kv)) return ATTN_ERR_UNSUPPORTED;
+  // The kernels address one (sequence, KV head) slab with 32-bit byte offsets.
+  if (int64_t(s.T_max) * s.D * elem_size(s.dt) >= (int64_t(1) << 31)) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 

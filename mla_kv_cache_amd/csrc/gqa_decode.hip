@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_util.h"
 #include "launch.h"
 
@@ -244,6 +246,256 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(
 // about G/2 dot2 + G/64 exps, which is what matters when G = 4..8.
 constexpr int kPoRows = 64;
 
+template <int N, class F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, F, I + 1>(static_cast<F&&>(f));
+  }
+}
+
+// Hand-scheduled blocks of DPP arithmetic (inline assembly). The compiler
+// inserts the wait states that gfx950 needs between dependent instructions
+// for the code it generates, but it cannot see into inline assembly, so each
+// block carries its own, as measured on the part:
+//  * a VALU write followed by a DPP read of that VGPR needs two wait states;
+//  * a VALU write followed by v_permlane16/32_swap reading it needs two;
+//  * a v_dot2c_f32_bf16 result read by any other VALU instruction needs
+//    three, while a following v_dot2c accumulating into the same register
+//    needs none.
+// Every block therefore opens with s_nop 1 (covering whatever the compiler
+// wrote just before) and closes with enough wait states for whatever the
+// compiler reads just after; inside a block the spacing is explicit.
+
+// acc[h] += dot(q_h, k) over the four bf16 pairs of one 16-byte K chunk, for
+// G heads: query word e of the chunk for head h is the value that lane L0 + e
+// of the caller's 16-lane row holds in qr[h] (row_newbcast source operand).
+template <int L0>
+__device__ __forceinline__ void dot_chunk2(float (&acc)[2], const uint32_t (&qr)[2], const uint4& k) {
+  asm("s_nop 1\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %2, %4 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %3, %4 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %2, %5 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %3, %5 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %2, %6 row_newbcast:%10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %3, %6 row_newbcast:%10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %2, %7 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %3, %7 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 2"
+      : "+v"(acc[0]), "+v"(acc[1])
+      : "v"(qr[0]), "v"(qr[1]), "v"(k.x), "v"(k.y), "v"(k.z), "v"(k.w), "i"(L0 + 0), "i"(L0 + 1), "i"(L0 + 2), "i"(L0 + 3));
+}
+
+template <int L0>
+__device__ __forceinline__ void dot_chunk4(float (&acc)[4], const uint32_t (&qr)[4], const uint4& k) {
+  asm("s_nop 1\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %4, %8 row_newbcast:%12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %5, %8 row_newbcast:%12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %6, %8 row_newbcast:%12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %7, %8 row_newbcast:%12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %4, %9 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %5, %9 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %6, %9 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %7, %9 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %4, %10 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %5, %10 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %6, %10 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %7, %10 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %4, %11 row_newbcast:%15 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %5, %11 row_newbcast:%15 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %6, %11 row_newbcast:%15 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %7, %11 row_newbcast:%15 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 2"
+      : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+      : "v"(qr[0]), "v"(qr[1]), "v"(qr[2]), "v"(qr[3]), "v"(k.x), "v"(k.y), "v"(k.z), "v"(k.w), "i"(L0 + 0), "i"(L0 + 1), "i"(L0 + 2), "i"(L0 + 3));
+}
+
+template <int L0>
+__device__ __forceinline__ void dot_chunk8(float (&acc)[8], const uint32_t (&qr)[8], const uint4& k) {
+  asm("s_nop 1\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %8, %16 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %9, %16 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %10, %16 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %11, %16 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %4, %12, %16 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %5, %13, %16 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %6, %14, %16 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %7, %15, %16 row_newbcast:%20 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %8, %17 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %9, %17 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %10, %17 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %11, %17 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %4, %12, %17 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %5, %13, %17 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %6, %14, %17 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %7, %15, %17 row_newbcast:%21 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %8, %18 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %9, %18 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %10, %18 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %11, %18 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %4, %12, %18 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %5, %13, %18 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %6, %14, %18 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %7, %15, %18 row_newbcast:%22 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %8, %19 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %1, %9, %19 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %2, %10, %19 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %3, %11, %19 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %4, %12, %19 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %5, %13, %19 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %6, %14, %19 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %7, %15, %19 row_newbcast:%23 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 2"
+      : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6]), "+v"(acc[7])
+      : "v"(qr[0]), "v"(qr[1]), "v"(qr[2]), "v"(qr[3]), "v"(qr[4]), "v"(qr[5]), "v"(qr[6]), "v"(qr[7]), "v"(k.x), "v"(k.y), "v"(k.z), "v"(k.w), "i"(L0 + 0), "i"(L0 + 1), "i"(L0 + 2), "i"(L0 + 3));
+}
+
+// Maximum over all 64 lanes of N values per lane (four DPP steps inside each
+// 16-lane row, then the two row swaps); every lane ends with the results.
+__device__ __forceinline__ void wave_max4(float (&x)[4]) {
+  float t[4];
+  asm("s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %2, %2, %2 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %3, %3, %3 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %2, %2, %2 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %3, %3, %3 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %2, %2, %2 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %3, %3, %3 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %2, %2, %2 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %3, %3, %3 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_mov_b32 %4, %0\n\t"
+      "v_mov_b32 %5, %1\n\t"
+      "v_mov_b32 %6, %2\n\t"
+      "v_mov_b32 %7, %3\n\t"
+      "s_nop 1\n\t"
+      "v_permlane16_swap_b32 %0, %4\n\t"
+      "v_permlane16_swap_b32 %1, %5\n\t"
+      "v_permlane16_swap_b32 %2, %6\n\t"
+      "v_permlane16_swap_b32 %3, %7\n\t"
+      "v_max_f32 %0, %0, %4\n\t"
+      "v_max_f32 %1, %1, %5\n\t"
+      "v_max_f32 %2, %2, %6\n\t"
+      "v_max_f32 %3, %3, %7\n\t"
+      "v_mov_b32 %4, %0\n\t"
+      "v_mov_b32 %5, %1\n\t"
+      "v_mov_b32 %6, %2\n\t"
+      "v_mov_b32 %7, %3\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %4\n\t"
+      "v_permlane32_swap_b32 %1, %5\n\t"
+      "v_permlane32_swap_b32 %2, %6\n\t"
+      "v_permlane32_swap_b32 %3, %7\n\t"
+      "v_max_f32 %0, %0, %4\n\t"
+      "v_max_f32 %1, %1, %5\n\t"
+      "v_max_f32 %2, %2, %6\n\t"
+      "v_max_f32 %3, %3, %7\n\t"
+      "s_nop 1"
+      : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]));
+}
+
+__device__ __forceinline__ void wave_max8(float (&x)[8]) {
+  float t[8];
+  asm("s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %2, %2, %2 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %3, %3, %3 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %4, %4, %4 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %5, %5, %5 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %6, %6, %6 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %7, %7, %7 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %2, %2, %2 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %3, %3, %3 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %4, %4, %4 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %5, %5, %5 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %6, %6, %6 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %7, %7, %7 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %2, %2, %2 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %3, %3, %3 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %4, %4, %4 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %5, %5, %5 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %6, %6, %6 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %7, %7, %7 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %2, %2, %2 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %3, %3, %3 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %4, %4, %4 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %5, %5, %5 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %6, %6, %6 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %7, %7, %7 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "v_mov_b32 %8, %0\n\t"
+      "v_mov_b32 %9, %1\n\t"
+      "v_mov_b32 %10, %2\n\t"
+      "v_mov_b32 %11, %3\n\t"
+      "v_mov_b32 %12, %4\n\t"
+      "v_mov_b32 %13, %5\n\t"
+      "v_mov_b32 %14, %6\n\t"
+      "v_mov_b32 %15, %7\n\t"
+      "s_nop 1\n\t"
+      "v_permlane16_swap_b32 %0, %8\n\t"
+      "v_permlane16_swap_b32 %1, %9\n\t"
+      "v_permlane16_swap_b32 %2, %10\n\t"
+      "v_permlane16_swap_b32 %3, %11\n\t"
+      "v_permlane16_swap_b32 %4, %12\n\t"
+      "v_permlane16_swap_b32 %5, %13\n\t"
+      "v_permlane16_swap_b32 %6, %14\n\t"
+      "v_permlane16_swap_b32 %7, %15\n\t"
+      "v_max_f32 %0, %0, %8\n\t"
+      "v_max_f32 %1, %1, %9\n\t"
+      "v_max_f32 %2, %2, %10\n\t"
+      "v_max_f32 %3, %3, %11\n\t"
+      "v_max_f32 %4, %4, %12\n\t"
+      "v_max_f32 %5, %5, %13\n\t"
+      "v_max_f32 %6, %6, %14\n\t"
+      "v_max_f32 %7, %7, %15\n\t"
+      "v_mov_b32 %8, %0\n\t"
+      "v_mov_b32 %9, %1\n\t"
+      "v_mov_b32 %10, %2\n\t"
+      "v_mov_b32 %11, %3\n\t"
+      "v_mov_b32 %12, %4\n\t"
+      "v_mov_b32 %13, %5\n\t"
+      "v_mov_b32 %14, %6\n\t"
+      "v_mov_b32 %15, %7\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %8\n\t"
+      "v_permlane32_swap_b32 %1, %9\n\t"
+      "v_permlane32_swap_b32 %2, %10\n\t"
+      "v_permlane32_swap_b32 %3, %11\n\t"
+      "v_permlane32_swap_b32 %4, %12\n\t"
+      "v_permlane32_swap_b32 %5, %13\n\t"
+      "v_permlane32_swap_b32 %6, %14\n\t"
+      "v_permlane32_swap_b32 %7, %15\n\t"
+      "v_max_f32 %0, %0, %8\n\t"
+      "v_max_f32 %1, %1, %9\n\t"
+      "v_max_f32 %2, %2, %10\n\t"
+      "v_max_f32 %3, %3, %11\n\t"
+      "v_max_f32 %4, %4, %12\n\t"
+      "v_max_f32 %5, %5, %13\n\t"
+      "v_max_f32 %6, %6, %14\n\t"
+      "v_max_f32 %7, %7, %15\n\t"
+      "s_nop 1"
+      : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7]));
+}
+
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
+// no swizzle, no stride): loads at or past num_records bytes return zeros.
+constexpr int kBufWord3 = 0x00020000;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
@@ -268,12 +520,22 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(
   if (start >= n) return;
   const int end = min(start, n - P) + P;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   const int rr = lane / LPR, c = lane % LPR;
   const int H = h_kv * G;
 
-  // Query of the G heads, read with uniform addresses (scalar loads).
+  // Query of the G heads as packed bf16 pairs. For G = 1 it is read with
+  // uniform addresses (scalar loads: it fits the scalar registers). For
+  // G >= 2 it would not, so it is spread over vector registers instead:
+  // word w sits in register w / 16 of lane w % 16 of every 16-lane row, and
+  // each dot product fetches it with a row broadcast (dot_chunk2/4/8).
+  constexpr bool kBcastQ = G >= 2;
+  constexpr int QR = kBcastQ ? G * D / 32 : 1;
   const uint32_t* qw = reinterpret_cast<const uint32_t*>(q + ((size_t)b * H + (size_t)j * G) * D);
+  uint32_t qd[QR];
+#pragma unroll
+  for (int r = 0; r < QR; ++r) qd[r] = kBcastQ ? qw[16 * r + (threadIdx.x & 15)] : 0u;
 
   float m[G], lpart[G], acc[G][8];
 #pragma unroll
@@ -284,30 +546,49 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
 
+  // Buffer resources over this (sequence, KV head) slab, limited to the
+  // sequence's valid rows: a read at or past row n returns zeros, so the
+  // tail of the last tile needs no clamping and padding rows are never
+  // fetched. Byte offsets fit 32 bits (the host limits T_max * D * 2).
   const size_t head_off = ((size_t)b * h_kv + j) * (size_t)T_max * D;
-  const uint16_t* kb = kc + head_off;
-  const uint16_t* vb = vc + head_off + (size_t)c * 8;
-  const uint32_t kt_lds = lds_addr(&ktile[wave][0]);
+  const int valid_bytes = n * (D * 2);
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + head_off), 0, valid_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + head_off), 0, valid_bytes, kBufWord3);
+  const uint32_t kt_lds = __builtin_amdgcn_readfirstlane(lds_addr(&ktile[wave][0]));
   const unsigned char* kt = &ktile[wave][0];
   float* wt = &wtab[wave][0][0];
 
-  // K tile -> LDS (slot = 64*i + lane holds row slot/CH, stored chunk slot%CH,
-  // which carries logical chunk (slot%CH) ^ (row % CH)).
+  // K tile -> LDS. Copy i moves rows RPC*i .. RPC*i + RPC - 1 of the tile (one
+  // KiB); its lane l fills LDS chunk 64*i + l, i.e. row RPC*i + l / CH, stored
+  // chunk l % CH, which carries logical chunk (l % CH) ^ (row % CH). The source
+  // offset inside the copy's KiB depends on i only through i % KPER.
+  constexpr int RPC = 1024 / (D * 2);           // rows per copy
+  constexpr int KPER = (RPC % CH == 0) ? 1 : CH / RPC;
+  uint32_t kvoff[KPER];
+#pragma unroll
+  for (int mm = 0; mm < KPER; ++mm) {
+    const int rl = lane / CH, pc = lane % CH;
+    const int lc = pc ^ ((RPC * mm + rl) % CH);
+    kvoff[mm] = (uint32_t)(rl * D + lc * 8) * 2u;
+  }
   auto copy_k = [&](int t0) {
-    const uint16_t* tbase = kb + (size_t)t0 * D;  // wave-uniform
-    // Partly unrolled on purpose: fully unrolled, the per-slot offsets are
-    // loop-invariant and get hoisted out of the tile loop, costing registers.
-#pragma unroll 4
+    const uint32_t tile_off = (uint32_t)t0 * (D * 2);
+#pragma unroll
     for (int i = 0; i < NK; ++i) {
-      const int slot = 64 * i + lane;
-      const int r = slot / CH, pc = slot % CH;
-      const int lc = pc ^ (r % CH);
-      const int rr_ = min(t0 + r, end - 1) - t0;
-      copy16_to_lds_sbase(kt_lds + 1024u * i, tbase, (uint32_t)(rr_ * D + lc * 8) * 2u);
+      const uint32_t soff = tile_off + 1024u * i;
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   ::"s"(kt_lds + 1024u * i), "v"(kvoff[i % KPER]), "s"(krs), "s"(soff)
+                   : "memory");
     }
   };
-  // V rows -> registers (row layout), one wave-wide load per RPI rows.
-  auto load_v = [&](int t0, int i) { return ld16(vb + (size_t)min(t0 + i * RPI + rr, end - 1) * D); };
+  // V rows -> registers (row layout): load i brings rows i*RPI .. i*RPI+RPI-1.
+  const uint32_t vvoff = (uint32_t)(rr * D + c * 8) * 2u;
+  auto load_v = [&](int t0, int i) {
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(vrs, vvoff, (uint32_t)t0 * (D * 2) + 1024u * i, 0);
+    return make_uint4(w.x, w.y, w.z, w.w);
+  };
 
   for (int t0 = start + wave * kPoRows; t0 < end; t0 += kWaves * kPoRows) {
     copy_k(t0);
@@ -323,25 +604,48 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(
     // ---- scores: lane owns position t0 + lane; its K row comes out of LDS
     // in one batch, then G dot products run on it.
     const unsigned char* krow = kt + lane * (D * 2);
-    uint4 kk[CH];
-#pragma unroll
-    for (int jc = 0; jc < CH; ++jc) kk[jc] = *reinterpret_cast<const uint4*>(krow + 16 * (jc ^ (lane % CH)));
     float s[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) s[h] = 0.f;
+    // The row is read from LDS in KS slices of CH / KS chunks, each used at
+    // once, so only one slice is held in registers beside the V tile.
+    constexpr int KS = G >= 4 ? 2 : 1;
+    constexpr int CS = CH / KS;
+    static_for<KS>([&](auto ks_) {
+      constexpr int ks = decltype(ks_)::value;
+      uint4 kk[CS];
 #pragma unroll
-    for (int jc = 0; jc < CH; ++jc) {
+      for (int u = 0; u < CS; ++u)
+        kk[u] = *reinterpret_cast<const uint4*>(krow + 16 * ((ks * CS + u) ^ (lane % CH)));
+      static_for<CS>([&](auto u_) {
+        constexpr int u = decltype(u_)::value;
+        constexpr int jc = ks * CS + u;
+        if constexpr (kBcastQ) {
+          // Query word h*D/2 + 4*jc + e is register (h*D/2 + 4*jc) / 16,
+          // row lane 4*(jc % 4) + e.
+          constexpr int l0 = 4 * (jc % 4);
+          uint32_t qr[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const uint32_t* qh = qw + h * (D / 2) + 4 * jc;
-        float a = s[h];
-        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[0]), __builtin_bit_cast(bf16x2, kk[jc].x), a, false);
-        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[1]), __builtin_bit_cast(bf16x2, kk[jc].y), a, false);
-        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[2]), __builtin_bit_cast(bf16x2, kk[jc].z), a, false);
-        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[3]), __builtin_bit_cast(bf16x2, kk[jc].w), a, false);
-        s[h] = a;
-      }
-    }
+          for (int h = 0; h < G; ++h) qr[h] = qd[(h * (D / 2) + 4 * jc) / 16];
+          if constexpr (G == 2) dot_chunk2<l0>(s, qr, kk[u]);
+          else if constexpr (G == 4) dot_chunk4<l0>(s, qr, kk[u]);
+          else dot_chunk8<l0>(s, qr, kk[u]);
+        } else {
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const uint32_t* qh = qw + h * (D / 2) + 4 * jc;
+            float a = s[h];
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[0]), __builtin_bit_cast(bf16x2, kk[u].x), a, false);
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[1]), __builtin_bit_cast(bf16x2, kk[u].y), a, false);
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[2]), __builtin_bit_cast(bf16x2, kk[u].z), a, false);
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[3]), __builtin_bit_cast(bf16x2, kk[u].w), a, false);
+            s[h] = a;
+          }
+        }
+      });
+      // Keep the next slice's reads below this slice's arithmetic.
+      __builtin_amdgcn_sched_barrier(0);
+    });
     // The K area is rewritten by the next tile's copy: all its reads are done.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const bool valid = t0 + lane < end;
@@ -350,9 +654,18 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       s[h] = valid ? s[h] * qk_scale_log2 : kNegInf;
-      mx[h] = wave_max(s[h]);
-      need |= mx[h] > m[h] + kTau;
+      mx[h] = s[h];
     }
+    if constexpr (G == 4) {
+      wave_max4(mx);
+    } else if constexpr (G == 8) {
+      wave_max8(mx);
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) mx[h] = wave_max(mx[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) need |= mx[h] > m[h] + kTau;
     if (need) {  // wave-uniform: the maxima are wave-wide
 #pragma unroll
       for (int h = 0; h < G; ++h) {

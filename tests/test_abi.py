@@ -110,6 +110,8 @@ def _gqa(lib, **kw):
     (dict(lens=NULL), INVALID), (dict(out=NULL), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
     (dict(T=(1 << 30) + 1), INVALID),
+    (dict(T=1 << 23, B=1, h_q=2, h_kv=1), UNSUPPORTED),   # one 2 GiB K slab: past 32-bit offsets
+    (dict(T=(1 << 23) - 1, B=1, h_q=2, h_kv=1, wsb=0), WORKSPACE),
     (dict(D=96), UNSUPPORTED), (dict(D=256), UNSUPPORTED),
     (dict(h_q=24, h_kv=1), UNSUPPORTED), (dict(h_q=96, h_kv=3), UNSUPPORTED),
     (dict(dt=7), UNSUPPORTED),

@@ -15,6 +15,10 @@ float64 on the exact input values (bf16 inputs are widened exactly):
 * ``attention.decode_mla`` -- absorbed multi-head latent attention: every
   head scores against one cached latent plus a decoupled rotary key, and
   averages the latent itself.
+* ``step.decode_gqa_step`` / ``step.decode_mla_step`` -- one decode step:
+  the new token's K/V (or latent) row is written at ``seq_lens[b]``, then the
+  token attends over the extended cache (``step.append_kv`` /
+  ``step.append_latent`` are the writes alone).
 * ``cache.kv_cache_bytes`` / ``cache.mla_cache_bytes`` -- the cache-size
   arithmetic.
 * ``brute`` -- pure-Python scalar loops for tiny shapes (a second,
@@ -33,5 +37,6 @@ from .attention import (  # noqa: F401
     decode_gqa_lse,
     clamp_len,
 )
+from .step import append_kv, append_latent, decode_gqa_step, decode_mla_step  # noqa: F401
 from .cache import kv_cache_bytes, mla_cache_bytes  # noqa: F401
 from . import brute  # noqa: F401

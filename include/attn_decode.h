@@ -4,7 +4,9 @@
  * One decode step: every sequence b of a batch has ONE new query token per
  * head, and every query head attends over the n = seq_lens[b] positions
  * already in its KV cache (the new token's own key/value included: the cache
- * is appended first, then attended). There is no mask inside [0, n).
+ * is appended first, then attended). There is no mask inside [0, n). The
+ * *_step entry points do the append themselves: there seq_lens[b] is the
+ * length before the step and the new row goes to position seq_lens[b].
  *
  *   MHA / GQA / MQA   h_q query heads share h_kv KV heads in consecutive
  *                     groups of g = h_q / h_kv: query head i reads KV head
@@ -124,6 +126,32 @@ int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
                     float scale, attn_dtype dt, void* out,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Decode step that first appends the new token ("Attention Variants: MHA,
+ * MQA, GQA — Speed vs Quality at Scale", section "The KV Cache Problem": each
+ * new token's K and V are stored in the cache, then the token attends over
+ * every cached pair, its own included).
+ * k_new, v_new [B, h_kv, D] dtype dt: the new token's key and value per KV head.
+ * Here seq_lens[b] is the cached length BEFORE the step. Row pos =
+ * max(seq_lens[b], 0) of KV head j of k_cache / v_cache receives k_new[b, j] /
+ * v_new[b, j] (bit-exact copies), then every query head attends over pos + 1
+ * positions, exactly as attn_decode_gqa would with seq_lens[b] + 1. A
+ * sequence whose cache is full (pos >= T_max) is not written and attends over
+ * its T_max cached positions. Only row pos of each head is written; seq_lens
+ * is not modified (advancing it is the caller's job). k_new and v_new must not
+ * overlap each other, the caches or any other argument (ATTN_ERR_INVALID_ARG).
+ * Same plan and workspace as attn_decode_gqa. */
+int attn_decode_gqa_step(const void* q, const void* k_new, const void* v_new,
+                         void* k_cache, void* v_cache, const int32_t* seq_lens,
+                         int B, int h_q, int h_kv, int D, int T_max, float scale, attn_dtype dt,
+                         void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The write of attn_decode_gqa_step alone, same rules (h_q = h_kv for the
+ * shape checks): k_new / v_new [B, h_kv, D] copied bit for bit into row
+ * max(seq_lens[b], 0) of each KV head unless the cache is full. */
+int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                   const int32_t* seq_lens, int B, int h_kv, int D, int T_max, attn_dtype dt,
+                   hipStream_t stream);
+
 /* Stage 1 alone, with an explicit partition_size P >= 1 and NP = ceil(T_max / P):
  * part_out [B, h_q, NP, D] fp32: softmax-weighted average of V over the valid
  *          positions of partition p, i.e. t in [p*P, min((p+1)*P, n));
@@ -162,6 +190,28 @@ int attn_decode_mla(const void* q_nope_absorbed, const void* q_rope, const void*
                     const int32_t* seq_lens, int B, int H, int d_c, int d_r, int T_max,
                     float scale, void* out, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
+
+/* Decode step that first appends the new token's cache row ("Attention
+ * variants: MQA, GQA, and MLA", section "MLA: cache a latent, not the keys
+ * and values": the new latent is concatenated to the cache, then the scores
+ * and the average run over the extended cache).
+ * latent_new [B, d_c+d_r] bf16: [latent | rotary key] of the new token.
+ * seq_lens[b] is the cached length BEFORE the step; row pos = max(seq_lens[b], 0)
+ * of latent_cache receives latent_new[b] (bit-exact copy), then every head
+ * attends over pos + 1 positions; a full cache (pos >= T_max) is not written
+ * and is attended over its T_max positions. seq_lens is not modified.
+ * latent_new must not overlap any other argument. Same workspace as
+ * attn_decode_mla. */
+int attn_decode_mla_step(const void* q_nope_absorbed, const void* q_rope, const void* latent_new,
+                         void* latent_cache, const int32_t* seq_lens, int B, int H, int d_c,
+                         int d_r, int T_max, float scale, void* out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* The write of attn_decode_mla_step alone: latent_new [B, d_c+d_r] bf16 copied
+ * bit for bit into row max(seq_lens[b], 0) of latent_cache unless it is full.
+ * Any d_c + d_r that is a multiple of 8. */
+int attn_latent_append(const void* latent_new, void* latent_cache, const int32_t* seq_lens,
+                       int B, int d_c, int d_r, int T_max, hipStream_t stream);
 
 /* Stage 1 alone; same partial layout as attn_decode_gqa_partial with h_q = H
  * and D = d_c. Merge with attn_decode_merge(..., Dv = d_c, out_dt = ATTN_BF16). */

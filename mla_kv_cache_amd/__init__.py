@@ -26,6 +26,7 @@ __all__ = [
     "attn_decode_gqa_partial", "attn_decode_merge",
     "attn_decode_mla_plan", "attn_decode_mla_workspace_bytes", "attn_decode_mla",
     "attn_decode_mla_partial",
+    "attn_decode_gqa_step", "attn_kv_append", "attn_decode_mla_step", "attn_latent_append",
 ]
 
 
@@ -148,6 +149,50 @@ def attn_decode_gqa(q, k_cache, v_cache, seq_lens, scale: Optional[float] = None
     return out
 
 
+def _new_rows(k_new, v_new, B, h_kv, D, dtype):
+    if tuple(k_new.shape) != (B, h_kv, D) or tuple(v_new.shape) != (B, h_kv, D):
+        raise ValueError(f"k_new and v_new must be [{B}, {h_kv}, {D}]")
+    if k_new.dtype != dtype or v_new.dtype != dtype:
+        raise TypeError("k_new and v_new must have the caches' dtype")
+
+
+def attn_decode_gqa_step(q, k_new, v_new, k_cache, v_cache, seq_lens, scale: Optional[float] = None,
+                         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Append k_new/v_new [B,h_kv,D] at row seq_lens[b] of the caches (in place), then attend
+    over seq_lens[b] + 1 positions. seq_lens (lengths before the step) is not modified.
+    Returns out [B, h_q, D] in q's dtype."""
+    B, h_q, h_kv, D, T_max = _gqa_shapes(q, k_cache, v_cache)
+    dev = _dev(q, k_new, v_new, k_cache, v_cache, seq_lens)
+    _lens(seq_lens, B)
+    _new_rows(k_new, v_new, B, h_kv, D, q.dtype)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    need = attn_decode_gqa_workspace_bytes(B, h_q, h_kv, D, T_max, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(out, workspace)
+    _check(load().attn_decode_gqa_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(seq_lens), B, h_q, h_kv, D, T_max, scale,
+                                       _dt(q), _ptr(out), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(dev)),
+           "attn_decode_gqa_step")
+    return out
+
+
+def attn_kv_append(k_new, v_new, k_cache, v_cache, seq_lens) -> None:
+    """Copy k_new/v_new [B,h_kv,D] into row seq_lens[b] of k_cache/v_cache (in place)."""
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("expected k_cache and v_cache [B,h_kv,T_max,D] of one dtype")
+    B, h_kv, T_max, D = k_cache.shape
+    dev = _dev(k_new, v_new, k_cache, v_cache, seq_lens)
+    _lens(seq_lens, B)
+    _new_rows(k_new, v_new, B, h_kv, D, k_cache.dtype)
+    _check(load().attn_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(seq_lens), B, h_kv, D, T_max, _dt(k_cache), _stream(dev)),
+           "attn_kv_append")
+
+
 def attn_decode_gqa_partial(q, k_cache, v_cache, seq_lens, partition_size: int,
                             scale: Optional[float] = None, part_out=None, part_lse=None):
     """Stage 1 with an explicit partition size. Returns (part_out [B,h_q,NP,D], part_lse [B,h_q,NP])."""
@@ -237,3 +282,40 @@ def attn_decode_mla_partial(q_nope_absorbed, q_rope, latent_cache, seq_lens, sca
                                           int(partition_size), _ptr(part_out), _ptr(part_lse),
                                           _stream(dev)), "attn_decode_mla_partial")
     return part_out, part_lse
+
+
+def attn_decode_mla_step(q_nope_absorbed, q_rope, latent_new, latent_cache, seq_lens, scale: float,
+                         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Append latent_new [B, d_c+d_r] at row seq_lens[b] of latent_cache (in place), then attend
+    over seq_lens[b] + 1 positions. Returns out [B, H, d_c] bf16."""
+    B, H, d_c, d_r, T_max = _mla_shapes(q_nope_absorbed, q_rope, latent_cache)
+    dev = _dev(q_nope_absorbed, q_rope, latent_new, latent_cache, seq_lens)
+    _lens(seq_lens, B)
+    if tuple(latent_new.shape) != (B, d_c + d_r) or latent_new.dtype != torch.bfloat16:
+        raise ValueError(f"latent_new must be bfloat16 [{B}, {d_c + d_r}]")
+    if out is None:
+        out = torch.empty((B, H, d_c), dtype=torch.bfloat16, device=dev)
+    need = attn_decode_mla_workspace_bytes(B, H, d_c, d_r, T_max)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(out, workspace)
+    _check(load().attn_decode_mla_step(_ptr(q_nope_absorbed), _ptr(q_rope), _ptr(latent_new),
+                                       _ptr(latent_cache), _ptr(seq_lens), B, H, d_c, d_r, T_max,
+                                       float(scale), _ptr(out), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(dev)),
+           "attn_decode_mla_step")
+    return out
+
+
+def attn_latent_append(latent_new, latent_cache, seq_lens, d_c: int = 512) -> None:
+    """Copy latent_new [B, d_c+d_r] into row seq_lens[b] of latent_cache [B,T_max,d_c+d_r] (in place)."""
+    if latent_cache.dim() != 3 or latent_cache.dtype != torch.bfloat16:
+        raise ValueError("expected a bfloat16 latent_cache [B, T_max, d_c + d_r]")
+    B, T_max, W = latent_cache.shape
+    dev = _dev(latent_new, latent_cache, seq_lens)
+    _lens(seq_lens, B)
+    if tuple(latent_new.shape) != (B, W) or latent_new.dtype != torch.bfloat16:
+        raise ValueError(f"latent_new must be bfloat16 [{B}, {W}]")
+    _check(load().attn_latent_append(_ptr(latent_new), _ptr(latent_cache), _ptr(seq_lens), B,
+                                     int(d_c), W - int(d_c), T_max, _stream(dev)),
+           "attn_latent_append")

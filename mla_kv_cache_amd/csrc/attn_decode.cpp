@@ -98,6 +98,46 @@ int mla_auto_partition(const MlaShape& s) {
   return P;
 }
 
+// The new rows of a decode step ([B, h_kv, D] each) must not overlap the
+// caches they are written into, each other, or any other argument buffer.
+int check_new_rows(const GqaShape& s, const void* k_new, const void* v_new, const void* q,
+                   const void* k, const void* v, const int32_t* lens, const void* out,
+                   size_t out_b, const void* ws, size_t ws_b) {
+  if (!k_new || !v_new) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return ATTN_ERR_UNSUPPORTED;
+  const size_t es = elem_size(s.dt);
+  const size_t nb = size_t(s.B) * s.h_kv * s.D * es;
+  const size_t kb = size_t(s.B) * s.h_kv * size_t(s.T_max) * s.D * es;
+  const size_t qb = q ? size_t(s.B) * s.h_q * s.D * es : 0;
+  for (const void* x : {k_new, v_new}) {
+    if (overlap(x, nb, k, kb) || overlap(x, nb, v, kb) || overlap(x, nb, lens, size_t(s.B) * 4) ||
+        overlap(x, nb, out, out_b) || overlap(x, nb, ws, ws_b))
+      return ATTN_ERR_INVALID_ARG;
+  }
+  if (overlap(k_new, nb, v_new, nb) || overlap(k, kb, v, kb) || overlap(q, qb, k, kb) ||
+      overlap(q, qb, v, kb) || overlap(lens, size_t(s.B) * 4, k, kb) ||
+      overlap(lens, size_t(s.B) * 4, v, kb))
+    return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+// Same for the new latent rows of an MLA decode step ([B, d_c + d_r]).
+int check_new_latent(const MlaShape& s, const void* lat_new, const void* qn, const void* qr,
+                     const void* lat, const int32_t* lens, const void* out, size_t out_b,
+                     const void* ws, size_t ws_b) {
+  if (!lat_new) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(lat_new)) return ATTN_ERR_UNSUPPORTED;
+  const size_t row = size_t(s.d_c + s.d_r) * 2;
+  const size_t nb = size_t(s.B) * row, lb = size_t(s.B) * size_t(s.T_max) * row;
+  const size_t qnb = size_t(s.B) * s.H * s.d_c * 2, qrb = size_t(s.B) * s.H * s.d_r * 2;
+  if (overlap(lat_new, nb, lat, lb) || overlap(lat_new, nb, lens, size_t(s.B) * 4) ||
+      overlap(lat_new, nb, out, out_b) || overlap(lat_new, nb, ws, ws_b) ||
+      overlap(qn, qnb, lat, lb) || overlap(qr, qrb, lat, lb) ||
+      overlap(lens, size_t(s.B) * 4, lat, lb))
+    return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
 int set_plan(int P, int T_max, size_t ws, int* partition_size, int* num_partitions,
              size_t* workspace_bytes) {
   if (partition_size) *partition_size = P;
@@ -187,11 +227,9 @@ int attn_decode_gqa_partial(const void* q, const void* k_cache, const void* v_ca
   if (!part_lse) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(part_lse)) return ATTN_ERR_UNSUPPORTED;
   if (overlap(part_out, ob, part_lse, size_t(B) * h_q * NP * sizeof(float))) return ATTN_ERR_INVALID_ARG;
-  const float sc = float(double(scale) * kLog2e);
-  if (attn::launch_gqa_partial(int(dt), D, h_q / h_kv, q, k_cache, v_cache, seq_lens, B, h_kv,
-                               T_max, partition_size, NP, sc, part_out, part_lse,
-                               stream) != hipSuccess)
-    return ATTN_ERR_HIP;
+  const attn::GqaArgs a{q, k_cache, v_cache, seq_lens, nullptr, nullptr, B, h_kv, T_max,
+                        partition_size, NP, float(double(scale) * kLog2e), part_out, part_lse};
+  if (attn::launch_gqa_partial(int(dt), D, h_q / h_kv, a, stream) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
 
@@ -209,15 +247,21 @@ int attn_decode_merge(const float* part_out, const float* part_lse, const int32_
   if (overlap(out, out_b, part_out, rows * NP * Dv * sizeof(float)) ||
       overlap(out, out_b, part_lse, rows * NP * sizeof(float)))
     return ATTN_ERR_INVALID_ARG;
-  if (attn::launch_merge(int(out_dt), part_out, part_lse, seq_lens, B, H, Dv, T_max,
+  if (attn::launch_merge(int(out_dt), part_out, part_lse, seq_lens, 0, B, H, Dv, T_max,
                          partition_size, NP, out, stream) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
 
-int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* seq_lens, int B, int h_q, int h_kv, int D, int T_max,
-                    float scale, attn_dtype dt, void* out, void* workspace,
+}  // extern "C"
+
+namespace {
+
+// Whole decode (k_new == nullptr) or decode step (append the new rows, then
+// attend) for the GQA family: partial kernels, then the merge.
+int gqa_decode_impl(const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                    const void* v_cache, const int32_t* seq_lens, int B, int h_q, int h_kv, int D,
+                    int T_max, float scale, attn_dtype dt, void* out, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
   const GqaShape s{B, h_q, h_kv, D, T_max, dt};
   int st = check_gqa_shape(s);
@@ -231,16 +275,60 @@ int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
   const size_t need = partial_bytes(int64_t(B) * h_q, NP, D);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
-  if (overlap(workspace, need, out, out_b)) return ATTN_ERR_INVALID_ARG;
+  const size_t kb = size_t(B) * h_kv * size_t(T_max) * D * elem_size(dt);
+  if (overlap(workspace, need, out, out_b) || overlap(workspace, need, k_cache, kb) ||
+      overlap(workspace, need, v_cache, kb))
+    return ATTN_ERR_INVALID_ARG;
+  if (k_new) {
+    st = check_new_rows(s, k_new, v_new, q, k_cache, v_cache, seq_lens, out, out_b, workspace, need);
+    if (st != ATTN_OK) return st;
+  }
   float* part_out = static_cast<float*>(workspace);
   float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                              align_up(size_t(B) * h_q * NP * D * sizeof(float)));
-  const float sc = float(double(scale) * kLog2e);
-  if (attn::launch_gqa_partial(int(dt), D, h_q / h_kv, q, k_cache, v_cache, seq_lens, B, h_kv,
-                               T_max, P, NP, sc, part_out, part_lse, stream) != hipSuccess)
+  const attn::GqaArgs a{q, k_cache, v_cache, seq_lens, k_new, v_new, B, h_kv, T_max, P, NP,
+                        float(double(scale) * kLog2e), part_out, part_lse};
+  if (attn::launch_gqa_partial(int(dt), D, h_q / h_kv, a, stream) != hipSuccess) return ATTN_ERR_HIP;
+  if (attn::launch_merge(int(dt), part_out, part_lse, seq_lens, k_new ? 1 : 0, B, h_q, D, T_max,
+                         P, NP, out, stream) != hipSuccess)
     return ATTN_ERR_HIP;
-  if (attn::launch_merge(int(dt), part_out, part_lse, seq_lens, B, h_q, D, T_max, P, NP, out,
-                         stream) != hipSuccess)
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* seq_lens, int B, int h_q, int h_kv, int D, int T_max,
+                    float scale, attn_dtype dt, void* out, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  return gqa_decode_impl(q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, h_q, h_kv, D, T_max,
+                         scale, dt, out, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_gqa_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                         void* v_cache, const int32_t* seq_lens, int B, int h_q, int h_kv, int D,
+                         int T_max, float scale, attn_dtype dt, void* out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (!k_new || !v_new) return ATTN_ERR_INVALID_ARG;
+  return gqa_decode_impl(q, k_new, v_new, k_cache, v_cache, seq_lens, B, h_q, h_kv, D, T_max,
+                         scale, dt, out, workspace, workspace_bytes, stream);
+}
+
+int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                   const int32_t* seq_lens, int B, int h_kv, int D, int T_max, attn_dtype dt,
+                   hipStream_t stream) {
+  const GqaShape s{B, h_kv, h_kv, D, T_max, dt};
+  int st = check_gqa_shape(s);
+  if (st != ATTN_OK) return st;
+  if (!k_new || !v_new || !k_cache || !v_cache || !seq_lens) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return ATTN_ERR_UNSUPPORTED;
+  st = check_new_rows(s, k_new, v_new, nullptr, k_cache, v_cache, seq_lens, nullptr, 0, nullptr, 0);
+  if (st != ATTN_OK) return st;
+  if (attn::launch_kv_append(int(dt), k_new, v_new, k_cache, v_cache, seq_lens, B, h_kv, D, T_max,
+                             stream) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -292,16 +380,19 @@ int attn_decode_mla_partial(const void* q_nope, const void* q_rope, const void* 
   if (!part_lse) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(part_lse)) return ATTN_ERR_UNSUPPORTED;
   if (overlap(part_out, ob, part_lse, size_t(B) * H * NP * sizeof(float))) return ATTN_ERR_INVALID_ARG;
-  const float sc = float(double(scale) * kLog2e);
-  if (attn::launch_mla_partial(q_nope, q_rope, latent, seq_lens, B, H, T_max, partition_size, NP,
-                               sc, part_out, part_lse, stream) != hipSuccess)
-    return ATTN_ERR_HIP;
+  const attn::MlaArgs a{q_nope, q_rope, latent, seq_lens, nullptr, B, H, T_max, partition_size, NP,
+                        float(double(scale) * kLog2e), part_out, part_lse};
+  if (attn::launch_mla_partial(a, stream) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
 
-int attn_decode_mla(const void* q_nope, const void* q_rope, const void* latent,
-                    const int32_t* seq_lens, int B, int H, int d_c, int d_r, int T_max,
-                    float scale, void* out, void* workspace, size_t workspace_bytes,
+}  // extern "C"
+
+namespace {
+
+int mla_decode_impl(const void* q_nope, const void* q_rope, const void* lat_new,
+                    const void* latent, const int32_t* seq_lens, int B, int H, int d_c, int d_r,
+                    int T_max, float scale, void* out, void* workspace, size_t workspace_bytes,
                     hipStream_t stream) {
   const MlaShape s{B, H, d_c, d_r, T_max};
   int st = check_mla_shape(s);
@@ -315,16 +406,60 @@ int attn_decode_mla(const void* q_nope, const void* q_rope, const void* latent,
   const size_t need = partial_bytes(int64_t(B) * H, NP, d_c);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
-  if (overlap(workspace, need, out, out_b)) return ATTN_ERR_INVALID_ARG;
+  const size_t lb = size_t(B) * size_t(T_max) * (d_c + d_r) * 2;
+  if (overlap(workspace, need, out, out_b) || overlap(workspace, need, latent, lb))
+    return ATTN_ERR_INVALID_ARG;
+  if (lat_new) {
+    st = check_new_latent(s, lat_new, q_nope, q_rope, latent, seq_lens, out, out_b, workspace, need);
+    if (st != ATTN_OK) return st;
+  }
   float* part_out = static_cast<float*>(workspace);
   float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                              align_up(size_t(B) * H * NP * d_c * sizeof(float)));
-  const float sc = float(double(scale) * kLog2e);
-  if (attn::launch_mla_partial(q_nope, q_rope, latent, seq_lens, B, H, T_max, P, NP, sc, part_out,
-                               part_lse, stream) != hipSuccess)
+  const attn::MlaArgs a{q_nope, q_rope, latent, seq_lens, lat_new, B, H, T_max, P, NP,
+                        float(double(scale) * kLog2e), part_out, part_lse};
+  if (attn::launch_mla_partial(a, stream) != hipSuccess) return ATTN_ERR_HIP;
+  if (attn::launch_merge(int(ATTN_BF16), part_out, part_lse, seq_lens, lat_new ? 1 : 0, B, H, d_c,
+                         T_max, P, NP, out, stream) != hipSuccess)
     return ATTN_ERR_HIP;
-  if (attn::launch_merge(int(ATTN_BF16), part_out, part_lse, seq_lens, B, H, d_c, T_max, P, NP,
-                         out, stream) != hipSuccess)
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_mla(const void* q_nope, const void* q_rope, const void* latent,
+                    const int32_t* seq_lens, int B, int H, int d_c, int d_r, int T_max,
+                    float scale, void* out, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  return mla_decode_impl(q_nope, q_rope, nullptr, latent, seq_lens, B, H, d_c, d_r, T_max, scale,
+                         out, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_mla_step(const void* q_nope, const void* q_rope, const void* latent_new,
+                         void* latent_cache, const int32_t* seq_lens, int B, int H, int d_c,
+                         int d_r, int T_max, float scale, void* out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (!latent_new) return ATTN_ERR_INVALID_ARG;
+  return mla_decode_impl(q_nope, q_rope, latent_new, latent_cache, seq_lens, B, H, d_c, d_r, T_max,
+                         scale, out, workspace, workspace_bytes, stream);
+}
+
+int attn_latent_append(const void* latent_new, void* latent_cache, const int32_t* seq_lens, int B,
+                       int d_c, int d_r, int T_max, hipStream_t stream) {
+  if (B < 1 || d_c < 1 || d_r < 0 || T_max < 1) return ATTN_ERR_INVALID_ARG;
+  if (T_max > kMaxTmax || B > kMaxGridYZ) return ATTN_ERR_INVALID_ARG;
+  if (int64_t(B) * T_max * (d_c + d_r) >= kMaxElems) return ATTN_ERR_INVALID_ARG;
+  if (!latent_new || !latent_cache || !seq_lens) return ATTN_ERR_INVALID_ARG;
+  if ((d_c + d_r) % 8 != 0) return ATTN_ERR_UNSUPPORTED;   // whole 16-byte pieces per row
+  if (!aligned16(latent_new) || !aligned16(latent_cache)) return ATTN_ERR_UNSUPPORTED;
+  const size_t nb = size_t(B) * (d_c + d_r) * 2, lb = size_t(B) * size_t(T_max) * (d_c + d_r) * 2;
+  if (overlap(latent_new, nb, latent_cache, lb) || overlap(latent_new, nb, seq_lens, size_t(B) * 4) ||
+      overlap(latent_cache, lb, seq_lens, size_t(B) * 4))
+    return ATTN_ERR_INVALID_ARG;
+  if (attn::launch_latent_append(latent_new, latent_cache, seq_lens, B, d_c + d_r, T_max, stream) !=
+      hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }

@@ -115,6 +115,31 @@ __device__ __forceinline__ void copy16_to_lds_sbase(uint32_t lds_base, const voi
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(base), "v"(voff), "s"(sbu) : "memory");
 }
 
+// 16-byte vector store. Every call site guarantees 16-byte alignment.
+__device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Number of positions a row attends over. seq_len is the cached length
+// (before the step when len_add = 1, a decode step that appends one row at
+// position max(seq_len, 0) when that position is below T_max).
+__device__ __forceinline__ int attended_len(int seq_len, int len_add, int T_max) {
+  const int pos = max(seq_len, 0);
+  return pos >= T_max ? T_max : min(pos + len_add, T_max);
+}
+
+// Decode step: copy one new cache row (ROW_BYTES, a multiple of 16) with the
+// threads of the work-group, then make it visible to every later read of the
+// work-group, including reads through the vector L1 and direct-to-LDS copies
+// (release fence, barrier, acquire fence). Call from uniform control flow.
+template <int ROW_BYTES>
+__device__ __forceinline__ void write_row_then_sync(void* dst, const void* src) {
+  static_assert(ROW_BYTES % 16 == 0, "rows are copied in 16-byte pieces");
+  for (int i = threadIdx.x; i < ROW_BYTES / 16; i += blockDim.x)
+    st16(static_cast<unsigned char*>(dst) + 16 * i, ld16(static_cast<const unsigned char*>(src) + 16 * i));
+  __threadfence();
+  __syncthreads();
+  __threadfence();
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)p;
 }

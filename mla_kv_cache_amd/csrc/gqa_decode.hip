@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "device_util.h"
@@ -70,22 +71,37 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kTau = 8.0f;
 
 template <class E, int D, int G>
-__global__ __launch_bounds__(kThreads) void gqa_partial_kernel(
-    const typename E::storage* __restrict__ q, const typename E::storage* __restrict__ kc,
-    const typename E::storage* __restrict__ vc, const int32_t* __restrict__ seq_lens, int h_kv,
-    int T_max, int P, int NP, float qk_scale_log2, float* __restrict__ part_out,
-    float* __restrict__ part_lse) {
+__global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const GqaArgs a) {
+  using S = typename E::storage;
   constexpr int EPL = E::EPL;
   constexpr int LPR = D / EPL;       // lanes per row
   constexpr int RPI = 64 / LPR;      // rows per wave-wide 16-byte load
   constexpr int NI = G >= 16 ? 2 : (G >= 8 ? 4 : 8);  // loads per block per tensor (bounded by registers)
   constexpr int RB = NI * RPI;       // rows per block per wave
+  const S* __restrict__ q = static_cast<const S*>(a.q);
+  // Not restrict: a decode step writes one row of each cache before reading.
+  const S* kc = static_cast<const S*>(a.k);
+  const S* vc = static_cast<const S*>(a.v);
+  float* __restrict__ part_out = a.part_out;
+  float* __restrict__ part_lse = a.part_lse;
+  const int h_kv = a.h_kv, T_max = a.T_max, P = a.P, NP = a.NP;
+  const float qk_scale_log2 = a.qk_scale_log2;
 
   const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  const int n = min(max(seq_lens[b], 0), T_max);
+  const int len0 = a.seq_lens[b];
+  const int n = attended_len(len0, a.k_new ? 1 : 0, T_max);
   const int start = p * P;
   if (start >= n) return;  // no position in this partition: nothing written, the merge skips it
   const int end = min(start, n - P) + P;  // = min(start + P, n) without overflow
+  if (a.k_new) {  // decode step: the work-group that reads the new row writes it first
+    const int pos = max(len0, 0);
+    if (pos < T_max && pos >= start && pos < end) {
+      const size_t row = (((size_t)b * h_kv + j) * (size_t)T_max + pos) * D;
+      const size_t src = ((size_t)b * h_kv + j) * D;
+      write_row_then_sync<D * sizeof(S)>(const_cast<S*>(kc) + row, static_cast<const S*>(a.k_new) + src);
+      write_row_then_sync<D * sizeof(S)>(const_cast<S*>(vc) + row, static_cast<const S*>(a.v_new) + src);
+    }
+  }
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rr = lane / LPR, c = lane % LPR;
@@ -497,11 +513,15 @@ constexpr int kBufWord3 = 0x00020000;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, const int32_t* __restrict__ seq_lens, int h_kv, int T_max,
-    int P, int NP, float qk_scale_log2, float* __restrict__ part_out,
-    float* __restrict__ part_lse) {
+__global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs a) {
+  const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
+  // Not restrict: a decode step writes one row of each cache before reading.
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v);
+  float* __restrict__ part_out = a.part_out;
+  float* __restrict__ part_lse = a.part_lse;
+  const int h_kv = a.h_kv, T_max = a.T_max, P = a.P, NP = a.NP;
+  const float qk_scale_log2 = a.qk_scale_log2;
   constexpr int CH = D / 8;              // 16-byte chunks per row
   constexpr int LPR = CH;                // lanes per row in the V layout
   constexpr int RPI = 64 / LPR;          // rows per wave-wide V load
@@ -515,10 +535,20 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(
   __shared__ __attribute__((aligned(16))) float wtab[kWaves][kPoRows][GP];
 
   const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  const int n = min(max(seq_lens[b], 0), T_max);
+  const int len0 = a.seq_lens[b];
+  const int n = attended_len(len0, a.k_new ? 1 : 0, T_max);
   const int start = p * P;
   if (start >= n) return;
   const int end = min(start, n - P) + P;
+  if (a.k_new) {  // decode step: the work-group that reads the new row writes it first
+    const int pos = max(len0, 0);
+    if (pos < T_max && pos >= start && pos < end) {
+      const size_t row = (((size_t)b * h_kv + j) * (size_t)T_max + pos) * D;
+      const size_t src = ((size_t)b * h_kv + j) * D;
+      write_row_then_sync<D * 2>(const_cast<uint16_t*>(kc) + row, static_cast<const uint16_t*>(a.k_new) + src);
+      write_row_then_sync<D * 2>(const_cast<uint16_t*>(vc) + row, static_cast<const uint16_t*>(a.v_new) + src);
+    }
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
@@ -760,25 +790,14 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(
 }
 
 template <int D, int G>
-hipError_t launch_po(const void* q, const void* k, const void* v, const int32_t* lens, int B,
-                     int h_kv, int T_max, int P, int NP, float sc, float* po, float* pl,
-                     hipStream_t stream) {
-  dim3 grid(NP, h_kv, B);
-  hipLaunchKernelGGL((gqa_partial_po_kernel<D, G>), grid, dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), lens, h_kv, T_max, P, NP, sc, po, pl);
+hipError_t launch_po(const GqaArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((gqa_partial_po_kernel<D, G>), dim3(a.NP, a.h_kv, a.B), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 template <class E, int D, int G>
-hipError_t launch_one(const void* q, const void* k, const void* v, const int32_t* lens, int B,
-                      int h_kv, int T_max, int P, int NP, float sc, float* po, float* pl,
-                      hipStream_t stream) {
-  using S = typename E::storage;
-  dim3 grid(NP, h_kv, B);
-  hipLaunchKernelGGL((gqa_partial_kernel<E, D, G>), grid, dim3(kThreads), 0, stream,
-                     static_cast<const S*>(q), static_cast<const S*>(k), static_cast<const S*>(v),
-                     lens, h_kv, T_max, P, NP, sc, po, pl);
+hipError_t launch_one(const GqaArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((gqa_partial_kernel<E, D, G>), dim3(a.NP, a.h_kv, a.B), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -789,27 +808,48 @@ hipError_t launch_one(const void* q, const void* k, const void* v, const int32_t
 constexpr int kPoMinGroup = ATTN_PO_MIN_GROUP;
 
 template <class E, int D>
-hipError_t launch_d(int G, const void* q, const void* k, const void* v, const int32_t* lens, int B,
-                    int h_kv, int T_max, int P, int NP, float sc, float* po, float* pl,
-                    hipStream_t s) {
+hipError_t launch_d(int G, const GqaArgs& a, hipStream_t s) {
   if constexpr (sizeof(typename E::storage) == 2) {
     if (G >= kPoMinGroup) {
       switch (G) {
-        case 1: return launch_po<D, 1>(q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
-        case 2: return launch_po<D, 2>(q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
-        case 4: return launch_po<D, 4>(q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
-        case 8: return launch_po<D, 8>(q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
+        case 1: return launch_po<D, 1>(a, s);
+        case 2: return launch_po<D, 2>(a, s);
+        case 4: return launch_po<D, 4>(a, s);
+        case 8: return launch_po<D, 8>(a, s);
         default: break;
       }
     }
   }
   switch (G) {
-    case 1: return launch_one<E, D, 1>(q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
-    case 2: return launch_one<E, D, 2>(q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
-    case 4: return launch_one<E, D, 4>(q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
-    case 8: return launch_one<E, D, 8>(q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
-    case 16: return launch_one<E, D, 16>(q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
+    case 1: return launch_one<E, D, 1>(a, s);
+    case 2: return launch_one<E, D, 2>(a, s);
+    case 4: return launch_one<E, D, 4>(a, s);
+    case 8: return launch_one<E, D, 8>(a, s);
+    case 16: return launch_one<E, D, 16>(a, s);
     default: return hipErrorInvalidValue;
+  }
+}
+
+// One thread per 16-byte piece of the new rows: piece i of row (b, j) goes to
+// row seq_lens[b] of head j of both caches. A full cache is left unchanged.
+__global__ __launch_bounds__(256) void kv_append_kernel(const unsigned char* __restrict__ k_new,
+                                                        const unsigned char* __restrict__ v_new,
+                                                        unsigned char* __restrict__ kc,
+                                                        unsigned char* __restrict__ vc,
+                                                        const int32_t* __restrict__ seq_lens,
+                                                        int B, int h_kv, int row_pieces, int T_max) {
+  const int64_t total = (int64_t)B * h_kv * row_pieces;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t bj = t / row_pieces;
+    const int piece = (int)(t % row_pieces);
+    const int b = (int)(bj / h_kv);
+    const int pos = max(seq_lens[b], 0);
+    if (pos >= T_max) continue;
+    const size_t dst = ((size_t)bj * T_max + pos) * row_pieces * 16 + (size_t)piece * 16;
+    const size_t src = (size_t)t * 16;
+    st16(kc + dst, ld16(k_new + src));
+    st16(vc + dst, ld16(v_new + src));
   }
 }
 
@@ -820,17 +860,28 @@ bool gqa_supported(int dt, int D, int group) {
   return (dt == 0 || dt == 1) && (D == 64 || D == 128) && g_ok;
 }
 
-hipError_t launch_gqa_partial(int dt, int D, int group, const void* q, const void* k,
-                              const void* v, const int32_t* lens, int B, int h_kv, int T_max,
-                              int P, int NP, float sc, float* po, float* pl, hipStream_t s) {
+hipError_t launch_gqa_partial(int dt, int D, int group, const GqaArgs& a, hipStream_t s) {
   if (dt == 1) {
-    if (D == 128) return launch_d<BF16Elem, 128>(group, q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
-    if (D == 64) return launch_d<BF16Elem, 64>(group, q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
+    if (D == 128) return launch_d<BF16Elem, 128>(group, a, s);
+    if (D == 64) return launch_d<BF16Elem, 64>(group, a, s);
   } else if (dt == 0) {
-    if (D == 128) return launch_d<F32Elem, 128>(group, q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
-    if (D == 64) return launch_d<F32Elem, 64>(group, q, k, v, lens, B, h_kv, T_max, P, NP, sc, po, pl, s);
+    if (D == 128) return launch_d<F32Elem, 128>(group, a, s);
+    if (D == 64) return launch_d<F32Elem, 64>(group, a, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_kv_append(int dt, const void* k_new, const void* v_new, void* k, void* v,
+                            const int32_t* seq_lens, int B, int h_kv, int D, int T_max,
+                            hipStream_t s) {
+  const int row_pieces = D * (dt == 1 ? 2 : 4) / 16;
+  const int64_t total = (int64_t)B * h_kv * row_pieces;
+  const int blocks = (int)std::min<int64_t>((total + 255) / 256, 4096);
+  hipLaunchKernelGGL(kv_append_kernel, dim3(blocks), dim3(256), 0, s,
+                     static_cast<const unsigned char*>(k_new), static_cast<const unsigned char*>(v_new),
+                     static_cast<unsigned char*>(k), static_cast<unsigned char*>(v), seq_lens, B, h_kv,
+                     row_pieces, T_max);
+  return hipGetLastError();
 }
 
 }  // namespace attn

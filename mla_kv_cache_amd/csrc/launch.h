@@ -10,22 +10,52 @@ namespace attn {
 // dt: 0 = fp32 storage, 1 = bf16 storage (values of attn_dtype).
 bool gqa_supported(int dt, int D, int group);
 
-hipError_t launch_gqa_partial(int dt, int D, int group, const void* q, const void* k,
-                              const void* v, const int32_t* seq_lens, int B, int h_kv,
-                              int T_max, int P, int NP, float qk_scale_log2,
-                              float* part_out, float* part_lse, hipStream_t stream);
+// Arguments of the GQA partial kernels (passed by value as kernel arguments).
+struct GqaArgs {
+  const void* q;              // [B, h_q, D]
+  const void* k;              // [B, h_kv, T_max, D]; written only in a decode step
+  const void* v;
+  const int32_t* seq_lens;    // [B]
+  const void* k_new;          // decode step: [B, h_kv, D] rows appended at seq_lens[b]
+  const void* v_new;          //   before attending; nullptr: plain decode
+  int B, h_kv, T_max, P, NP;
+  float qk_scale_log2;        // scale * log2(e)
+  float* part_out;            // [B, h_q, NP, D]
+  float* part_lse;            // [B, h_q, NP]
+};
+
+hipError_t launch_gqa_partial(int dt, int D, int group, const GqaArgs& a, hipStream_t stream);
+
+// Plain copy of the new K/V rows into the caches (the decode step's write alone).
+hipError_t launch_kv_append(int dt, const void* k_new, const void* v_new, void* k, void* v,
+                            const int32_t* seq_lens, int B, int h_kv, int D, int T_max,
+                            hipStream_t stream);
 
 bool merge_supported(int out_dt, int Dv);
 
+// len_add = 1 for a decode step: each row attends over min(max(seq_lens[b], 0) + 1, T_max)
+// positions instead of min(max(seq_lens[b], 0), T_max).
 hipError_t launch_merge(int out_dt, const float* part_out, const float* part_lse,
-                        const int32_t* seq_lens, int B, int H, int Dv, int T_max, int P,
-                        int NP, void* out, hipStream_t stream);
+                        const int32_t* seq_lens, int len_add, int B, int H, int Dv, int T_max,
+                        int P, int NP, void* out, hipStream_t stream);
 
 bool mla_supported(int H, int d_c, int d_r);
 
-hipError_t launch_mla_partial(const void* q_nope, const void* q_rope, const void* latent,
-                              const int32_t* seq_lens, int B, int H, int T_max, int P, int NP,
-                              float qk_scale_log2, float* part_out, float* part_lse,
-                              hipStream_t stream);
+struct MlaArgs {
+  const void* q_nope;         // [B, H, 512]
+  const void* q_rope;         // [B, H, 64]
+  const void* latent;         // [B, T_max, 576]; written only in a decode step
+  const int32_t* seq_lens;    // [B]
+  const void* lat_new;        // decode step: [B, 576] rows appended at seq_lens[b]; nullptr: plain decode
+  int B, H, T_max, P, NP;
+  float qk_scale_log2;
+  float* part_out;            // [B, H, NP, 512]
+  float* part_lse;            // [B, H, NP]
+};
+
+hipError_t launch_mla_partial(const MlaArgs& a, hipStream_t stream);
+
+hipError_t launch_latent_append(const void* lat_new, void* latent, const int32_t* seq_lens,
+                                int B, int row_elems, int T_max, hipStream_t stream);
 
 }  // namespace attn

@@ -5,7 +5,13 @@
 // The full-row softmax average is sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M)
 // with M = max_p lse_p: the plain softmax regrouped by partition, nothing
 // approximated. Only the ceil(n / P) partitions that hold positions are read.
-// One work-group per row, 4 consecutive output elements per thread.
+//
+// One wave per row, four rows per work-group. Lane l owns VW consecutive
+// output elements of each 64*VW-wide slice of the row; the partitions are
+// walked four at a time with independent loads so that several partials of
+// a lane are in flight together. M and the normaliser come from a wave-wide
+// pass over the log-sum-exps; each partition's weight is then recomputed
+// from its (wave-uniform) log-sum-exp where it is used.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -16,52 +22,112 @@
 namespace attn {
 namespace {
 
-constexpr int kMergeThreads = 128;
+constexpr int kRowsPerGroup = 4;
 
-__device__ __forceinline__ void store4(float* o, float a, float b, float c, float d) {
-  *reinterpret_cast<float4*>(o) = make_float4(a, b, c, d);
+template <int VW>
+struct Vec;
+template <>
+struct Vec<1> {
+  typedef float type;
+  static __device__ __forceinline__ float get(const type& v, int i) { (void)i; return v; }
+};
+template <>
+struct Vec<2> {
+  typedef float2 type;
+  static __device__ __forceinline__ float get(const type& v, int i) { return i == 0 ? v.x : v.y; }
+};
+template <>
+struct Vec<4> {
+  typedef float4 type;
+  static __device__ __forceinline__ float get(const type& v, int i) {
+    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+  }
+};
+
+template <int VW>
+__device__ __forceinline__ void store_out(float* o, const float (&x)[VW]) {
+#pragma unroll
+  for (int i = 0; i < VW; ++i) o[i] = x[i];
 }
-__device__ __forceinline__ void store4(uint16_t* o, float a, float b, float c, float d) {
-  uint2 u;
-  u.x = (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
-  u.y = (uint32_t)f32_to_bf16_rne(c) | ((uint32_t)f32_to_bf16_rne(d) << 16);
-  *reinterpret_cast<uint2*>(o) = u;
+template <int VW>
+__device__ __forceinline__ void store_out(uint16_t* o, const float (&x)[VW]) {
+#pragma unroll
+  for (int i = 0; i < VW; ++i) o[i] = f32_to_bf16_rne(x[i]);
 }
 
-template <typename TO>
-__global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
+template <typename TO, int VW>
+__global__ __launch_bounds__(64 * kRowsPerGroup) void lse_merge_kernel(
     const float* __restrict__ part_out, const float* __restrict__ part_lse,
-    const int32_t* __restrict__ seq_lens, int H, int Dv, int T_max, int P, int NP,
-    TO* __restrict__ out) {
-  const int row = blockIdx.x;  // b * H + h
+    const int32_t* __restrict__ seq_lens, int len_add, int rows, int H, int Dv, int T_max, int P,
+    int NP, TO* __restrict__ out) {
+  using V = Vec<VW>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = blockIdx.x * kRowsPerGroup + wave;  // b * H + h, uniform in the wave
+  if (row >= rows) return;
   const int b = row / H;
-  const int n = min(max(seq_lens[b], 0), T_max);
+  const int n = attended_len(seq_lens[b], len_add, T_max);
   const int npv = n / P + (n % P != 0);
   const float* lse = part_lse + (size_t)row * NP;
   const float* po = part_out + (size_t)row * NP * Dv;
   TO* o = out + (size_t)row * Dv;
 
   float M = kNegInf;
-  for (int p = 0; p < npv; ++p) M = fmaxf(M, lse[p]);
+  for (int p = lane; p < npv; p += 64) M = fmaxf(M, lse[p]);
+  M = wave_max(M);
   float W = 0.f;
-  for (int p = 0; p < npv; ++p) W += fast_exp2(lse[p] - M);
+  for (int p = lane; p < npv; p += 64) W += fast_exp2(lse[p] - M);
+  const float invW = 1.f / wave_sum(W);
 
-  for (int d = threadIdx.x * 4; d < Dv; d += kMergeThreads * 4) {
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int p = 0; p < npv; ++p) {
-      const float w = fast_exp2(lse[p] - M);
-      const float4 x = *reinterpret_cast<const float4*>(po + (size_t)p * Dv + d);
-      a0 = fmaf(w, x.x, a0);
-      a1 = fmaf(w, x.y, a1);
-      a2 = fmaf(w, x.z, a2);
-      a3 = fmaf(w, x.w, a3);
+  for (int d0 = lane * VW; d0 < Dv; d0 += 64 * VW) {
+    float acc[4][VW];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < VW; ++i) acc[u][i] = 0.f;
+    int p = 0;
+    for (; p + 4 <= npv; p += 4) {
+      typename V::type x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        x[u] = *reinterpret_cast<const typename V::type*>(po + (size_t)(p + u) * Dv + d0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = fast_exp2(lse[p + u] - M) * invW;
+#pragma unroll
+        for (int i = 0; i < VW; ++i) acc[u][i] = fmaf(w, V::get(x[u], i), acc[u][i]);
+      }
     }
-    if (npv == 0) {
-      store4(o + d, 0.f, 0.f, 0.f, 0.f);
-    } else {
-      store4(o + d, a0 / W, a1 / W, a2 / W, a3 / W);
+    for (; p < npv; ++p) {
+      const typename V::type x = *reinterpret_cast<const typename V::type*>(po + (size_t)p * Dv + d0);
+      const float w = fast_exp2(lse[p] - M) * invW;
+#pragma unroll
+      for (int i = 0; i < VW; ++i) acc[0][i] = fmaf(w, V::get(x, i), acc[0][i]);
     }
+    float r[VW];
+#pragma unroll
+    for (int i = 0; i < VW; ++i) r[i] = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+    store_out<VW>(o + d0, r);  // npv == 0: the sums are empty and the row is zeros
   }
+}
+
+template <typename TO>
+hipError_t launch_typed(const float* part_out, const float* part_lse, const int32_t* seq_lens,
+                        int len_add, int B, int H, int Dv, int T_max, int P, int NP, TO* out,
+                        hipStream_t stream) {
+  const int rows = B * H;
+  const dim3 grid((unsigned)((rows + kRowsPerGroup - 1) / kRowsPerGroup));
+  const dim3 block(64 * kRowsPerGroup);
+  if (Dv % 256 == 0)
+    hipLaunchKernelGGL((lse_merge_kernel<TO, 4>), grid, block, 0, stream, part_out, part_lse,
+                       seq_lens, len_add, rows, H, Dv, T_max, P, NP, out);
+  else if (Dv % 128 == 0)
+    hipLaunchKernelGGL((lse_merge_kernel<TO, 2>), grid, block, 0, stream, part_out, part_lse,
+                       seq_lens, len_add, rows, H, Dv, T_max, P, NP, out);
+  else
+    hipLaunchKernelGGL((lse_merge_kernel<TO, 1>), grid, block, 0, stream, part_out, part_lse,
+                       seq_lens, len_add, rows, H, Dv, T_max, P, NP, out);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -71,17 +137,13 @@ bool merge_supported(int out_dt, int Dv) {
 }
 
 hipError_t launch_merge(int out_dt, const float* part_out, const float* part_lse,
-                        const int32_t* seq_lens, int B, int H, int Dv, int T_max, int P, int NP,
-                        void* out, hipStream_t stream) {
-  const dim3 grid((unsigned)B * (unsigned)H);
-  if (out_dt == 0) {
-    hipLaunchKernelGGL(lse_merge_kernel<float>, grid, dim3(kMergeThreads), 0, stream, part_out,
-                       part_lse, seq_lens, H, Dv, T_max, P, NP, static_cast<float*>(out));
-  } else {
-    hipLaunchKernelGGL(lse_merge_kernel<uint16_t>, grid, dim3(kMergeThreads), 0, stream, part_out,
-                       part_lse, seq_lens, H, Dv, T_max, P, NP, static_cast<uint16_t*>(out));
-  }
-  return hipGetLastError();
+                        const int32_t* seq_lens, int len_add, int B, int H, int Dv, int T_max,
+                        int P, int NP, void* out, hipStream_t stream) {
+  if (out_dt == 0)
+    return launch_typed(part_out, part_lse, seq_lens, len_add, B, H, Dv, T_max, P, NP,
+                        static_cast<float*>(out), stream);
+  return launch_typed(part_out, part_lse, seq_lens, len_add, B, H, Dv, T_max, P, NP,
+                      static_cast<uint16_t*>(out), stream);
 }
 
 }  // namespace attn

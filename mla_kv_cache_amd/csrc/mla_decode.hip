@@ -144,11 +144,15 @@ __device__ __forceinline__ void wait_tile_barrier(bool next_in_flight) {
 }
 
 template <int NHB>
-__global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(
-    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
-    const uint16_t* __restrict__ lat, const int32_t* __restrict__ seq_lens, int H, int T_max,
-    int P, int NP, float qk_scale_log2, float* __restrict__ part_out,
-    float* __restrict__ part_lse) {
+__global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(const MlaArgs a) {
+  const uint16_t* __restrict__ q_nope = static_cast<const uint16_t*>(a.q_nope);
+  const uint16_t* __restrict__ q_rope = static_cast<const uint16_t*>(a.q_rope);
+  // Not restrict: a decode step writes one row of the cache before reading.
+  const uint16_t* lat = static_cast<const uint16_t*>(a.latent);
+  float* __restrict__ part_out = a.part_out;
+  float* __restrict__ part_lse = a.part_lse;
+  const int H = a.H, T_max = a.T_max, P = a.P, NP = a.NP;
+  const float qk_scale_log2 = a.qk_scale_log2;
   constexpr int NWAVES = 2 * NHB;
   // Three tile buffers as separate objects: the copies of the next two tiles
   // are in flight while one is computed, and the compiler can tell the copy
@@ -160,10 +164,17 @@ __global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char xbuf[NWAVES * 4096];
 
   const int p = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;
-  const int n = min(max(seq_lens[b], 0), T_max);
+  const int len0 = a.seq_lens[b];
+  const int n = attended_len(len0, a.lat_new ? 1 : 0, T_max);
   const int start = p * P;
   if (start >= n) return;
   const int end = min(start, n - P) + P;
+  if (a.lat_new) {  // decode step: every work-group that reads the new row writes it first
+    const int pos = max(len0, 0);
+    if (pos < T_max && pos >= start && pos < end)
+      write_row_then_sync<kRow * 2>(const_cast<uint16_t*>(lat) + ((size_t)b * T_max + pos) * kRow,
+                                    static_cast<const uint16_t*>(a.lat_new) + (size_t)b * kRow);
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kh = wave & 1;             // half of the contraction / of the output dims
@@ -331,20 +342,47 @@ bool mla_supported(int H, int d_c, int d_r) {
   return d_c == kDc && d_r == kDr && H >= 32 && H % 32 == 0 && (H <= 128 || H % 128 == 0);
 }
 
-hipError_t launch_mla_partial(const void* q_nope, const void* q_rope, const void* latent,
-                              const int32_t* seq_lens, int B, int H, int T_max, int P, int NP,
-                              float sc, float* part_out, float* part_lse, hipStream_t stream) {
-  const int nhb = H >= 128 ? 4 : H / 32;  // 32-head blocks per work-group
-  const dim3 grid(NP, H / (32 * nhb), B);
-  const auto* qn = static_cast<const uint16_t*>(q_nope);
-  const auto* qr = static_cast<const uint16_t*>(q_rope);
-  const auto* lt = static_cast<const uint16_t*>(latent);
+hipError_t launch_mla_partial(const MlaArgs& a, hipStream_t stream) {
+  const int nhb = a.H >= 128 ? 4 : a.H / 32;  // 32-head blocks per work-group
+  const dim3 grid(a.NP, a.H / (32 * nhb), a.B);
   switch (nhb) {
-    case 4: hipLaunchKernelGGL(mla_partial_kernel<4>, grid, dim3(512), 0, stream, qn, qr, lt, seq_lens, H, T_max, P, NP, sc, part_out, part_lse); break;
-    case 3: hipLaunchKernelGGL(mla_partial_kernel<3>, grid, dim3(384), 0, stream, qn, qr, lt, seq_lens, H, T_max, P, NP, sc, part_out, part_lse); break;
-    case 2: hipLaunchKernelGGL(mla_partial_kernel<2>, grid, dim3(256), 0, stream, qn, qr, lt, seq_lens, H, T_max, P, NP, sc, part_out, part_lse); break;
-    default: hipLaunchKernelGGL(mla_partial_kernel<1>, grid, dim3(128), 0, stream, qn, qr, lt, seq_lens, H, T_max, P, NP, sc, part_out, part_lse); break;
+    case 4: hipLaunchKernelGGL(mla_partial_kernel<4>, grid, dim3(512), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(mla_partial_kernel<3>, grid, dim3(384), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(mla_partial_kernel<2>, grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL(mla_partial_kernel<1>, grid, dim3(128), 0, stream, a); break;
   }
+  return hipGetLastError();
+}
+
+namespace {
+
+// One thread per 16-byte piece of the new rows: row b goes to row seq_lens[b]
+// of sequence b. A full cache is left unchanged.
+__global__ __launch_bounds__(256) void latent_append_kernel(const unsigned char* __restrict__ lat_new,
+                                                            unsigned char* __restrict__ lat,
+                                                            const int32_t* __restrict__ seq_lens,
+                                                            int B, int row_pieces, int T_max) {
+  const int64_t total = (int64_t)B * row_pieces;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int b = (int)(t / row_pieces);
+    const int piece = (int)(t % row_pieces);
+    const int pos = max(seq_lens[b], 0);
+    if (pos >= T_max) continue;
+    st16(lat + ((size_t)b * T_max + pos) * row_pieces * 16 + (size_t)piece * 16, ld16(lat_new + (size_t)t * 16));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_latent_append(const void* lat_new, void* latent, const int32_t* seq_lens, int B,
+                                int row_elems, int T_max, hipStream_t stream) {
+  const int row_pieces = row_elems * 2 / 16;
+  const int64_t total = (int64_t)B * row_pieces;
+  const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+  hipLaunchKernelGGL(latent_append_kernel, dim3(blocks), dim3(256), 0, stream,
+                     static_cast<const unsigned char*>(lat_new), static_cast<unsigned char*>(latent),
+                     seq_lens, B, row_pieces, T_max);
   return hipGetLastError();
 }
 

@@ -188,3 +188,36 @@ def test_full_size_plans_fill_the_chip(lib):
         assert lib.attn_decode_gqa_plan(B, hq, hkv, 128, T, BF16, ctypes.byref(P), ctypes.byref(NP),
                                         None) == OK
         assert B * hkv * NP.value >= 1024        # at least 4 work-groups per CU on 256 CUs
+
+
+def test_step_and_append_argument_checks(lib):
+    f = lib.attn_decode_gqa_step
+    KN, VN = ctypes.c_void_p(1 << 46), ctypes.c_void_p(1 << 47)
+
+    def step(**kw):
+        a = dict(q=P16, kn=KN, vn=VN, k=P16b, v=P16c, lens=LENS, B=2, h_q=8, h_kv=2, D=128, T=1024,
+                 scale=0.1, dt=BF16, out=OUT, ws=WS, wsb=1 << 30)
+        a.update(kw)
+        return f(a["q"], a["kn"], a["vn"], a["k"], a["v"], a["lens"], a["B"], a["h_q"], a["h_kv"],
+                 a["D"], a["T"], a["scale"], a["dt"], a["out"], a["ws"], a["wsb"], None)
+
+    assert step(kn=NULL) == INVALID
+    assert step(vn=NULL) == INVALID
+    assert step(kn=P16b) == INVALID                       # new rows inside the K cache
+    assert step(vn=KN) == INVALID                         # k_new and v_new overlap
+    assert step(kn=ctypes.c_void_p((1 << 46) + 8)) == UNSUPPORTED
+    assert step(ws=P16b) == INVALID                       # workspace inside the K cache
+    assert step(wsb=16) == WORKSPACE
+    assert step(D=96) == UNSUPPORTED
+    a = lib.attn_kv_append
+    assert a(NULL, VN, P16b, P16c, LENS, 2, 2, 128, 1024, BF16, None) == INVALID
+    assert a(KN, VN, P16b, P16b, LENS, 2, 2, 128, 1024, BF16, None) == INVALID   # K and V caches overlap
+    assert a(KN, VN, P16b, P16c, LENS, 2, 2, 100, 1024, BF16, None) == UNSUPPORTED
+    m = lib.attn_decode_mla_step
+    LN = ctypes.c_void_p(1 << 46)
+    assert m(P16, P16b, NULL, P16c, LENS, 4, 128, 512, 64, 4096, 0.07, OUT, WS, 1 << 30, None) == INVALID
+    assert m(P16, P16b, P16c, P16c, LENS, 4, 128, 512, 64, 4096, 0.07, OUT, WS, 1 << 30, None) == INVALID
+    la = lib.attn_latent_append
+    assert la(NULL, P16c, LENS, 4, 512, 64, 4096, None) == INVALID
+    assert la(LN, P16c, LENS, 4, 512, 60, 4096, None) == UNSUPPORTED          # row not whole 16-byte pieces
+    assert la(P16c, P16c, LENS, 4, 512, 64, 4096, None) == INVALID            # new row inside the cache

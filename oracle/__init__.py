@@ -19,6 +19,8 @@ float64 on the exact input values (bf16 inputs are widened exactly):
   the new token's K/V (or latent) row is written at ``seq_lens[b]``, then the
   token attends over the extended cache (``step.append_kv`` /
   ``step.append_latent`` are the writes alone).
+* ``window.decode_gqa_window`` -- sliding-window decode: each row attends over
+  its last ``window`` cached positions.
 * ``cache.kv_cache_bytes`` / ``cache.mla_cache_bytes`` -- the cache-size
   arithmetic.
 * ``brute`` -- pure-Python scalar loops for tiny shapes (a second,
@@ -38,5 +40,6 @@ from .attention import (  # noqa: F401
     clamp_len,
 )
 from .step import append_kv, append_latent, decode_gqa_step, decode_mla_step  # noqa: F401
+from .window import decode_gqa_window, window_start  # noqa: F401
 from .cache import kv_cache_bytes, mla_cache_bytes  # noqa: F401
 from . import brute  # noqa: F401

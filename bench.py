@@ -161,6 +161,69 @@ def write_traffic(fetch_csv: str, write_csv: str, command: str):
     print(json.dumps(res, indent=1))
 
 
+# ----------------------------------------------------------------------------- widened rows
+
+def _time_calls(fn, stream, warmup, iters):
+    """Average HIP-event time (us) of one library call (all its kernels) on the launch stream."""
+    import torch
+    for _ in range(max(1, warmup)):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(iters):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / iters
+
+
+def time_next_rows(m, W, dev, stream, items, warmup, iters):
+    """Time the rows built beside the decode path, on the bench's own inputs (not in `value`):
+    the decode step that appends the new row (GQA g=8, MLA) and sliding-window decode."""
+    import torch
+    res = {}
+    by = {it["name"]: it for it in items}
+    if "gqa8" in by:
+        it = by["gqa8"]
+        w = it["w"]
+        q, k, v, lens = it["gpu"]
+        before = (lens - 1).to(torch.int32)
+        idx = (torch.arange(w.B, device=dev), slice(None), (lens - 1).long())
+        kn, vn = k[idx].clone(), v[idx].clone()         # re-append the last row: the cache stays as it was
+        ws = torch.empty(m.attn_decode_gqa_workspace_bytes(w.B, w.h_q, w.h_kv, w.D, w.T_max, w.dtype),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q)
+        us = _time_calls(lambda: m.attn_decode_gqa_step(q, kn, vn, k, v, before, w.scale, out, ws),
+                         stream, warmup, iters)
+        res["gqa8_step"] = {"workload": w.name + ", append + attend", "us": round(us, 2),
+                            "kv_GBps": round(it["kv"] / (us * 1e-6) / 1e9, 1)}
+        for window in (4096,):
+            span = int(sum(min(int(x), window) for x in lens.tolist()))
+            kvb = 2 * w.h_kv * w.D * 2 * span
+            wsw = torch.empty(m.attn_decode_gqa_workspace_bytes(w.B, w.h_q, w.h_kv, w.D, window, w.dtype),
+                              dtype=torch.uint8, device=dev)
+            us = _time_calls(lambda: m.attn_decode_gqa_window(q, k, v, lens, window, w.scale, out, wsw),
+                             stream, warmup, iters)
+            res[f"gqa8_window{window}"] = {"workload": w.name + f", sliding window {window}",
+                                           "us": round(us, 2), "kv_bytes": kvb,
+                                           "kv_GBps": round(kvb / (us * 1e-6) / 1e9, 1)}
+    if "mla" in by:
+        it = by["mla"]
+        w = it["w"]
+        qn, qr, lat, lens = it["gpu"]
+        before = (lens - 1).to(torch.int32)
+        new = lat[torch.arange(w.B, device=dev), (lens - 1).long()].clone()
+        ws = torch.empty(m.attn_decode_mla_workspace_bytes(w.B, w.H, w.d_c, w.d_r, w.T_max),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty((w.B, w.H, w.d_c), dtype=torch.bfloat16, device=dev)
+        us = _time_calls(lambda: m.attn_decode_mla_step(qn, qr, new, lat, before, w.scale, out, ws),
+                         stream, warmup, iters)
+        res["mla_step"] = {"workload": w.name + ", append + attend", "us": round(us, 2),
+                           "kv_GBps": round(it["kv"] / (us * 1e-6) / 1e9, 1)}
+    return res
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(items, budget_s=15.0):
@@ -205,6 +268,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--skip-mha", action="store_true", help="do not time the MHA breakdown workload")
+    ap.add_argument("--skip-next", action="store_true",
+                    help="do not time the decode-step and sliding-window variants")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run plain 1 GiB device copies (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -285,7 +350,7 @@ def main():
             src = os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "mla_decode.hip")
         items.append(dict(name=name, kind=kind, w=w, partial=partial, merge=merge, kv=kv,
                           other=other, flops=flops, P=P, NP=NP, kname=kname, src=src,
-                          in_step=name != "mha7b"))
+                          in_step=name != "mha7b", gpu=gpu))
         if name != "mha7b":
             cpu_items.append((name, kind, w, cpu))
         else:
@@ -364,6 +429,9 @@ def main():
             "kv_frac_hbm_peak": round(it["kv"] / ((p_ms + m_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "note": "timed alone, not part of the step",
         }
+
+    if not args.skip_next:
+        breakdown["next_rows"] = time_next_rows(m, W, dev, stream, items, args.warmup, args.steps)
 
     step_kv = sum(it["kv"] for it in step_items)
     value = step_kv / (ms_per_step * 1e-3) / 1e9

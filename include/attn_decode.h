@@ -126,6 +126,19 @@ int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
                     float scale, attn_dtype dt, void* out,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Sliding-window decode ("Grouped-Query Attention: Fewer KV Heads, Same
+ * Quality", section "GQA and Related KV-Head Choices in Modern Architectures":
+ * Mistral 7B pairs grouped KV heads with a window of w = 4096 positions). Each
+ * row attends over the last `window` of its n positions, t in
+ * [max(0, n - window), n); window >= n is the full decode. window >= 1.
+ * Positions before the window are never read. Workspace: at least
+ * attn_decode_gqa_workspace_bytes(B, h_q, h_kv, D, min(window, T_max), dt)
+ * bytes (the plan covers the window's span only). */
+int attn_decode_gqa_window(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seq_lens, int B, int h_q, int h_kv, int D, int T_max,
+                           int window, float scale, attn_dtype dt, void* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Decode step that first appends the new token ("Attention Variants: MHA,
  * MQA, GQA — Speed vs Quality at Scale", section "The KV Cache Problem": each
  * new token's K and V are stored in the cache, then the token attends over

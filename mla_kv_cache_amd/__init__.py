@@ -27,6 +27,7 @@ __all__ = [
     "attn_decode_mla_plan", "attn_decode_mla_workspace_bytes", "attn_decode_mla",
     "attn_decode_mla_partial",
     "attn_decode_gqa_step", "attn_kv_append", "attn_decode_mla_step", "attn_latent_append",
+    "attn_decode_gqa_window",
 ]
 
 
@@ -146,6 +147,28 @@ def attn_decode_gqa(q, k_cache, v_cache, seq_lens, scale: Optional[float] = None
                                   h_kv, D, T_max, scale, dt, _ptr(out), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(dev)),
            "attn_decode_gqa")
+    return out
+
+
+def attn_decode_gqa_window(q, k_cache, v_cache, seq_lens, window: int, scale: Optional[float] = None,
+                           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Sliding-window decode: each row attends over its last `window` positions.
+    Returns out [B, h_q, D] in q's dtype."""
+    B, h_q, h_kv, D, T_max = _gqa_shapes(q, k_cache, v_cache)
+    dev = _dev(q, k_cache, v_cache, seq_lens)
+    _lens(seq_lens, B)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    window = int(window)
+    need = attn_decode_gqa_workspace_bytes(B, h_q, h_kv, D, max(1, min(window, T_max)), q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(out, workspace)
+    _check(load().attn_decode_gqa_window(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B,
+                                         h_q, h_kv, D, T_max, window, scale, _dt(q), _ptr(out),
+                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _stream(dev)), "attn_decode_gqa_window")
     return out
 
 

@@ -50,6 +50,8 @@ SIGNATURES = {
     "attn_decode_mla_step": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                       _c_float, _vp, _vp, _c_size, _vp]),
     "attn_latent_append": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "attn_decode_gqa_window": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                        _c_int, _c_float, _c_int, _vp, _vp, _c_size, _vp]),
 }
 
 _lock = threading.Lock()

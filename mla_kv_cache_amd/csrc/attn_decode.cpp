@@ -227,7 +227,7 @@ int attn_decode_gqa_partial(const void* q, const void* k_cache, const void* v_ca
   if (!part_lse) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(part_lse)) return ATTN_ERR_UNSUPPORTED;
   if (overlap(part_out, ob, part_lse, size_t(B) * h_q * NP * sizeof(float))) return ATTN_ERR_INVALID_ARG;
-  const attn::GqaArgs a{q, k_cache, v_cache, seq_lens, nullptr, nullptr, B, h_kv, T_max,
+  const attn::GqaArgs a{q, k_cache, v_cache, seq_lens, nullptr, nullptr, 0, B, h_kv, T_max,
                         partition_size, NP, float(double(scale) * kLog2e), part_out, part_lse};
   if (attn::launch_gqa_partial(int(dt), D, h_q / h_kv, a, stream) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
@@ -247,7 +247,7 @@ int attn_decode_merge(const float* part_out, const float* part_lse, const int32_
   if (overlap(out, out_b, part_out, rows * NP * Dv * sizeof(float)) ||
       overlap(out, out_b, part_lse, rows * NP * sizeof(float)))
     return ATTN_ERR_INVALID_ARG;
-  if (attn::launch_merge(int(out_dt), part_out, part_lse, seq_lens, 0, B, H, Dv, T_max,
+  if (attn::launch_merge(int(out_dt), part_out, part_lse, seq_lens, 0, 0, B, H, Dv, T_max,
                          partition_size, NP, out, stream) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
@@ -261,17 +261,20 @@ namespace {
 // attend) for the GQA family: partial kernels, then the merge.
 int gqa_decode_impl(const void* q, const void* k_new, const void* v_new, const void* k_cache,
                     const void* v_cache, const int32_t* seq_lens, int B, int h_q, int h_kv, int D,
-                    int T_max, float scale, attn_dtype dt, void* out, void* workspace,
+                    int T_max, int window, float scale, attn_dtype dt, void* out, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
   const GqaShape s{B, h_q, h_kv, D, T_max, dt};
   int st = check_gqa_shape(s);
   if (st != ATTN_OK) return st;
-  if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (!isfinite(scale) || window < 0) return ATTN_ERR_INVALID_ARG;
   const size_t out_b = size_t(B) * h_q * D * elem_size(dt);
   st = check_gqa_ptrs(s, q, k_cache, v_cache, seq_lens, out, out_b);
   if (st != ATTN_OK) return st;
-  const int P = gqa_auto_partition(s);
-  const int NP = ceil_div(T_max, P);
+  // A window attends over at most `window` positions: plan for that span.
+  const int span = window > 0 && window < T_max ? window : T_max;
+  const GqaShape sp{B, h_q, h_kv, D, span, dt};
+  const int P = gqa_auto_partition(sp);
+  const int NP = ceil_div(span, P);
   const size_t need = partial_bytes(int64_t(B) * h_q, NP, D);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
@@ -286,11 +289,11 @@ int gqa_decode_impl(const void* q, const void* k_new, const void* v_new, const v
   float* part_out = static_cast<float*>(workspace);
   float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                              align_up(size_t(B) * h_q * NP * D * sizeof(float)));
-  const attn::GqaArgs a{q, k_cache, v_cache, seq_lens, k_new, v_new, B, h_kv, T_max, P, NP,
-                        float(double(scale) * kLog2e), part_out, part_lse};
+  const attn::GqaArgs a{q, k_cache, v_cache, seq_lens, k_new, v_new, window, B, h_kv, T_max, P,
+                        NP, float(double(scale) * kLog2e), part_out, part_lse};
   if (attn::launch_gqa_partial(int(dt), D, h_q / h_kv, a, stream) != hipSuccess) return ATTN_ERR_HIP;
-  if (attn::launch_merge(int(dt), part_out, part_lse, seq_lens, k_new ? 1 : 0, B, h_q, D, T_max,
-                         P, NP, out, stream) != hipSuccess)
+  if (attn::launch_merge(int(dt), part_out, part_lse, seq_lens, k_new ? 1 : 0, window, B, h_q, D,
+                         T_max, P, NP, out, stream) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -304,7 +307,16 @@ int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
                     float scale, attn_dtype dt, void* out, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
   return gqa_decode_impl(q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, h_q, h_kv, D, T_max,
-                         scale, dt, out, workspace, workspace_bytes, stream);
+                         0, scale, dt, out, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_gqa_window(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seq_lens, int B, int h_q, int h_kv, int D, int T_max,
+                           int window, float scale, attn_dtype dt, void* out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (window < 1) return ATTN_ERR_INVALID_ARG;
+  return gqa_decode_impl(q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, h_q, h_kv, D, T_max,
+                         window, scale, dt, out, workspace, workspace_bytes, stream);
 }
 
 int attn_decode_gqa_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
@@ -313,7 +325,7 @@ int attn_decode_gqa_step(const void* q, const void* k_new, const void* v_new, vo
                          size_t workspace_bytes, hipStream_t stream) {
   if (!k_new || !v_new) return ATTN_ERR_INVALID_ARG;
   return gqa_decode_impl(q, k_new, v_new, k_cache, v_cache, seq_lens, B, h_q, h_kv, D, T_max,
-                         scale, dt, out, workspace, workspace_bytes, stream);
+                         0, scale, dt, out, workspace, workspace_bytes, stream);
 }
 
 int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
@@ -419,8 +431,8 @@ int mla_decode_impl(const void* q_nope, const void* q_rope, const void* lat_new,
   const attn::MlaArgs a{q_nope, q_rope, latent, seq_lens, lat_new, B, H, T_max, P, NP,
                         float(double(scale) * kLog2e), part_out, part_lse};
   if (attn::launch_mla_partial(a, stream) != hipSuccess) return ATTN_ERR_HIP;
-  if (attn::launch_merge(int(ATTN_BF16), part_out, part_lse, seq_lens, lat_new ? 1 : 0, B, H, d_c,
-                         T_max, P, NP, out, stream) != hipSuccess)
+  if (attn::launch_merge(int(ATTN_BF16), part_out, part_lse, seq_lens, lat_new ? 1 : 0, 0, B, H,
+                         d_c, T_max, P, NP, out, stream) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }

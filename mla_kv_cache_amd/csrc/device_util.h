@@ -126,18 +126,24 @@ __device__ __forceinline__ int attended_len(int seq_len, int len_add, int T_max)
   return pos >= T_max ? T_max : min(pos + len_add, T_max);
 }
 
+// First attended position of a row of n positions (sliding window when window > 0).
+__device__ __forceinline__ int window_lo(int n, int window) { return window > 0 ? max(0, n - window) : 0; }
+
 // Decode step: copy one new cache row (ROW_BYTES, a multiple of 16) with the
 // threads of the work-group, then make it visible to every later read of the
-// work-group, including reads through the vector L1 and direct-to-LDS copies
-// (release fence, barrier, acquire fence). Call from uniform control flow.
+// same work-group (loads through the vector L1 and direct-to-LDS copies).
+// Writer and readers share one CU and its L1, so the work-group-scope release
+// and acquire around the barrier are enough; an agent-scope fence would write
+// back and invalidate the whole L2 of the XCD. No other work-group reads the
+// row in the same launch. Call from uniform control flow.
 template <int ROW_BYTES>
 __device__ __forceinline__ void write_row_then_sync(void* dst, const void* src) {
   static_assert(ROW_BYTES % 16 == 0, "rows are copied in 16-byte pieces");
   for (int i = threadIdx.x; i < ROW_BYTES / 16; i += blockDim.x)
     st16(static_cast<unsigned char*>(dst) + 16 * i, ld16(static_cast<const unsigned char*>(src) + 16 * i));
-  __threadfence();
-  __syncthreads();
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {

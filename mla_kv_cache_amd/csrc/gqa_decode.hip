@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const GqaArgs a) 
   const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int len0 = a.seq_lens[b];
   const int n = attended_len(len0, a.k_new ? 1 : 0, T_max);
-  const int start = p * P;
+  const int start = window_lo(n, a.window) + p * P;
   if (start >= n) return;  // no position in this partition: nothing written, the merge skips it
   const int end = min(start, n - P) + P;  // = min(start + P, n) without overflow
   if (a.k_new) {  // decode step: the work-group that reads the new row writes it first
@@ -537,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
   const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int len0 = a.seq_lens[b];
   const int n = attended_len(len0, a.k_new ? 1 : 0, T_max);
-  const int start = p * P;
+  const int start = window_lo(n, a.window) + p * P;
   if (start >= n) return;
   const int end = min(start, n - P) + P;
   if (a.k_new) {  // decode step: the work-group that reads the new row writes it first

@@ -18,6 +18,7 @@ struct GqaArgs {
   const int32_t* seq_lens;    // [B]
   const void* k_new;          // decode step: [B, h_kv, D] rows appended at seq_lens[b]
   const void* v_new;          //   before attending; nullptr: plain decode
+  int window;                 // > 0: attend over [max(0, n - window), n) only; 0: all of [0, n)
   int B, h_kv, T_max, P, NP;
   float qk_scale_log2;        // scale * log2(e)
   float* part_out;            // [B, h_q, NP, D]
@@ -34,10 +35,11 @@ hipError_t launch_kv_append(int dt, const void* k_new, const void* v_new, void* 
 bool merge_supported(int out_dt, int Dv);
 
 // len_add = 1 for a decode step: each row attends over min(max(seq_lens[b], 0) + 1, T_max)
-// positions instead of min(max(seq_lens[b], 0), T_max).
+// positions instead of min(max(seq_lens[b], 0), T_max). window > 0: only the last
+// `window` of those positions, partitioned from the first of them.
 hipError_t launch_merge(int out_dt, const float* part_out, const float* part_lse,
-                        const int32_t* seq_lens, int len_add, int B, int H, int Dv, int T_max,
-                        int P, int NP, void* out, hipStream_t stream);
+                        const int32_t* seq_lens, int len_add, int window, int B, int H, int Dv,
+                        int T_max, int P, int NP, void* out, hipStream_t stream);
 
 bool mla_supported(int H, int d_c, int d_r);
 

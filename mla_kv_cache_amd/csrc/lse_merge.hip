@@ -4,7 +4,8 @@
 // its positions, and lse_p = log2 sum_t exp(s_t) over the same positions.
 // The full-row softmax average is sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M)
 // with M = max_p lse_p: the plain softmax regrouped by partition, nothing
-// approximated. Only the ceil(n / P) partitions that hold positions are read.
+// approximated. Only the partitions that hold positions are read: ceil(n / P),
+// or ceil(min(n, window) / P) for a sliding window.
 //
 // One wave per row, four rows per work-group. Lane l owns VW consecutive
 // output elements of each 64*VW-wide slice of the row; the partitions are
@@ -58,8 +59,8 @@ __device__ __forceinline__ void store_out(uint16_t* o, const float (&x)[VW]) {
 template <typename TO, int VW>
 __global__ __launch_bounds__(64 * kRowsPerGroup) void lse_merge_kernel(
     const float* __restrict__ part_out, const float* __restrict__ part_lse,
-    const int32_t* __restrict__ seq_lens, int len_add, int rows, int H, int Dv, int T_max, int P,
-    int NP, TO* __restrict__ out) {
+    const int32_t* __restrict__ seq_lens, int len_add, int window, int rows, int H, int Dv,
+    int T_max, int P, int NP, TO* __restrict__ out) {
   using V = Vec<VW>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -67,7 +68,8 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void lse_merge_kernel(
   if (row >= rows) return;
   const int b = row / H;
   const int n = attended_len(seq_lens[b], len_add, T_max);
-  const int npv = n / P + (n % P != 0);
+  const int span = n - window_lo(n, window);
+  const int npv = span / P + (span % P != 0);
   const float* lse = part_lse + (size_t)row * NP;
   const float* po = part_out + (size_t)row * NP * Dv;
   TO* o = out + (size_t)row * Dv;
@@ -113,20 +115,20 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void lse_merge_kernel(
 
 template <typename TO>
 hipError_t launch_typed(const float* part_out, const float* part_lse, const int32_t* seq_lens,
-                        int len_add, int B, int H, int Dv, int T_max, int P, int NP, TO* out,
-                        hipStream_t stream) {
+                        int len_add, int window, int B, int H, int Dv, int T_max, int P, int NP,
+                        TO* out, hipStream_t stream) {
   const int rows = B * H;
   const dim3 grid((unsigned)((rows + kRowsPerGroup - 1) / kRowsPerGroup));
   const dim3 block(64 * kRowsPerGroup);
   if (Dv % 256 == 0)
     hipLaunchKernelGGL((lse_merge_kernel<TO, 4>), grid, block, 0, stream, part_out, part_lse,
-                       seq_lens, len_add, rows, H, Dv, T_max, P, NP, out);
+                       seq_lens, len_add, window, rows, H, Dv, T_max, P, NP, out);
   else if (Dv % 128 == 0)
     hipLaunchKernelGGL((lse_merge_kernel<TO, 2>), grid, block, 0, stream, part_out, part_lse,
-                       seq_lens, len_add, rows, H, Dv, T_max, P, NP, out);
+                       seq_lens, len_add, window, rows, H, Dv, T_max, P, NP, out);
   else
     hipLaunchKernelGGL((lse_merge_kernel<TO, 1>), grid, block, 0, stream, part_out, part_lse,
-                       seq_lens, len_add, rows, H, Dv, T_max, P, NP, out);
+                       seq_lens, len_add, window, rows, H, Dv, T_max, P, NP, out);
   return hipGetLastError();
 }
 
@@ -137,12 +139,12 @@ bool merge_supported(int out_dt, int Dv) {
 }
 
 hipError_t launch_merge(int out_dt, const float* part_out, const float* part_lse,
-                        const int32_t* seq_lens, int len_add, int B, int H, int Dv, int T_max,
-                        int P, int NP, void* out, hipStream_t stream) {
+                        const int32_t* seq_lens, int len_add, int window, int B, int H, int Dv,
+                        int T_max, int P, int NP, void* out, hipStream_t stream) {
   if (out_dt == 0)
-    return launch_typed(part_out, part_lse, seq_lens, len_add, B, H, Dv, T_max, P, NP,
+    return launch_typed(part_out, part_lse, seq_lens, len_add, window, B, H, Dv, T_max, P, NP,
                         static_cast<float*>(out), stream);
-  return launch_typed(part_out, part_lse, seq_lens, len_add, B, H, Dv, T_max, P, NP,
+  return launch_typed(part_out, part_lse, seq_lens, len_add, window, B, H, Dv, T_max, P, NP,
                       static_cast<uint16_t*>(out), stream);
 }
 

@@ -221,3 +221,14 @@ def test_step_and_append_argument_checks(lib):
     assert la(NULL, P16c, LENS, 4, 512, 64, 4096, None) == INVALID
     assert la(LN, P16c, LENS, 4, 512, 60, 4096, None) == UNSUPPORTED          # row not whole 16-byte pieces
     assert la(P16c, P16c, LENS, 4, 512, 64, 4096, None) == INVALID            # new row inside the cache
+
+
+def test_window_argument_checks(lib):
+    f = lib.attn_decode_gqa_window
+    base = [P16, P16b, P16c, LENS, 2, 8, 2, 128, 1024]
+    assert f(*base, 0, 0.1, BF16, OUT, WS, 1 << 30, None) == INVALID        # window must be >= 1
+    assert f(*base, -4, 0.1, BF16, OUT, WS, 1 << 30, None) == INVALID
+    assert f(*base, 64, 0.1, BF16, OUT, WS, 16, None) == WORKSPACE
+    need = lib.attn_decode_gqa_workspace_bytes(2, 8, 2, 128, 64, BF16)
+    assert 0 < need < lib.attn_decode_gqa_workspace_bytes(2, 8, 2, 128, 1024, BF16)
+    assert f(*base, 64, 0.1, BF16, OUT, WS, need - 1, None) == WORKSPACE

@@ -41,25 +41,32 @@ def _table(block_table) -> np.ndarray:
     return np.asarray(block_table, dtype=np.int64)
 
 
+def _rows(block_table, b: int, n: int, page_size: int):
+    """(physical page, row inside it) of logical positions 0..n-1 of sequence b."""
+    t = np.arange(n)
+    return _table(block_table)[b, t // page_size], t % page_size
+
+
+def _index(pages, page, row):
+    """pages[page[i], ..., row[i], ...] for GQA ([P, H, ps, D]) or MLA ([P, ps, W]) pages,
+    gathered in the pages' own dtype and then widened."""
+    if torch is not None and isinstance(pages, torch.Tensor):
+        pi, ri = torch.as_tensor(page), torch.as_tensor(row)
+        return _f64(pages[pi, :, ri] if pages.dim() == 4 else pages[pi, ri])
+    x = np.asarray(pages)
+    return _f64(x[page, :, row] if x.ndim == 4 else x[page, row])
+
+
 def gather_kv(pages, block_table, b: int, n: int, page_size: int) -> np.ndarray:
     """Positions 0..n-1 of sequence b, in logical order: float64 [h_kv, n, D] (GQA pages)."""
-    table = _table(block_table)
-    rows = []
-    for t in range(n):
-        page = int(table[b, t // page_size])
-        rows.append(_f64(pages[page, :, t % page_size]))          # [h_kv, D]
-    if not rows:
-        return np.zeros((pages.shape[1], 0, pages.shape[3]))
-    return np.stack(rows, axis=1)
+    page, row = _rows(block_table, b, n, page_size)
+    return _index(pages, page, row).transpose(1, 0, 2)   # [n, h_kv, D] -> [h_kv, n, D]
 
 
 def gather_latent(pages, block_table, b: int, n: int, page_size: int) -> np.ndarray:
     """Positions 0..n-1 of sequence b, in logical order: float64 [n, d_c + d_r] (MLA pages)."""
-    table = _table(block_table)
-    rows = [_f64(pages[int(table[b, t // page_size]), t % page_size]) for t in range(n)]
-    if not rows:
-        return np.zeros((0, pages.shape[2]))
-    return np.stack(rows, axis=0)
+    page, row = _rows(block_table, b, n, page_size)
+    return _index(pages, page, row)
 
 
 def decode_gqa_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float, page_size: int):
@@ -96,18 +103,22 @@ def decode_mla_paged(q_nope, q_rope, latent_pages, block_table, seq_lens, scale:
 
 def append_kv_paged(k_pages, v_pages, block_table, k_new, v_new, seq_lens, page_size: int):
     """Pages after writing k_new[b] / v_new[b] ([h_kv, D]) at logical position seq_lens[b]
-    (clamped below at 0; a sequence whose pages are full is not written)."""
+    (clamped below at 0; a sequence whose pages are full, or whose table entry for that
+    position names no page, is not written)."""
     table = _table(block_table)
     T_max = table.shape[1] * page_size
     B = table.shape[0]
     lens = _lens(seq_lens, B)
     k_out = k_pages.clone() if torch is not None and isinstance(k_pages, torch.Tensor) else np.array(k_pages)
     v_out = v_pages.clone() if torch is not None and isinstance(v_pages, torch.Tensor) else np.array(v_pages)
+    num_pages = k_pages.shape[0]
     for b in range(B):
         pos = max(int(lens[b]), 0)
         if pos >= T_max:
             continue
         page = int(table[b, pos // page_size])
+        if not 0 <= page < num_pages:      # an entry that names no page: nothing is written
+            continue
         k_out[page, :, pos % page_size] = k_new[b]
         v_out[page, :, pos % page_size] = v_new[b]
     return k_out, v_out

@@ -180,7 +180,8 @@ def _time_calls(fn, stream, warmup, iters):
 
 def time_next_rows(m, W, dev, stream, items, warmup, iters):
     """Time the rows built beside the decode path, on the bench's own inputs (not in `value`):
-    the decode step that appends the new row (GQA g=8, MLA) and sliding-window decode."""
+    the decode step that appends the new row (GQA g=8, MLA), sliding-window decode and the
+    paged cache (the same caches in 64-position pages at permuted physical slots)."""
     import torch
     res = {}
     by = {it["name"]: it for it in items}
@@ -208,6 +209,21 @@ def time_next_rows(m, W, dev, stream, items, warmup, iters):
             res[f"gqa8_window{window}"] = {"workload": w.name + f", sliding window {window}",
                                            "us": round(us, 2), "kv_bytes": kvb,
                                            "kv_GBps": round(kvb / (us * 1e-6) / 1e9, 1)}
+        # paged: the same cache cut into 64-position pages at randomly permuted physical slots
+        ps = 64
+        npg = w.T_max // ps
+        perm = torch.randperm(w.B * npg, generator=torch.Generator().manual_seed(0)).to(dev)
+        def paginate(x):
+            pages = torch.empty((w.B * npg, w.h_kv, ps, w.D), dtype=x.dtype, device=dev)
+            pages[perm] = x.view(w.B, w.h_kv, npg, ps, w.D).transpose(1, 2).reshape(w.B * npg, w.h_kv, ps, w.D)
+            return pages
+        kp, vp = paginate(k), paginate(v)
+        table = perm.view(w.B, npg).to(torch.int32)
+        us = _time_calls(lambda: m.attn_decode_gqa_paged(q, kp, vp, table, lens, w.scale, out, ws),
+                         stream, warmup, iters)
+        res["gqa8_paged64"] = {"workload": w.name + ", 64-position pages, permuted", "us": round(us, 2),
+                               "kv_GBps": round(it["kv"] / (us * 1e-6) / 1e9, 1)}
+        del kp, vp
     if "mla" in by:
         it = by["mla"]
         w = it["w"]
@@ -221,6 +237,17 @@ def time_next_rows(m, W, dev, stream, items, warmup, iters):
                          stream, warmup, iters)
         res["mla_step"] = {"workload": w.name + ", append + attend", "us": round(us, 2),
                            "kv_GBps": round(it["kv"] / (us * 1e-6) / 1e9, 1)}
+        ps = 64
+        npg = w.T_max // ps
+        perm = torch.randperm(w.B * npg, generator=torch.Generator().manual_seed(1)).to(dev)
+        lp = torch.empty((w.B * npg, ps, w.d_c + w.d_r), dtype=lat.dtype, device=dev)
+        lp[perm] = lat.view(w.B * npg, ps, w.d_c + w.d_r)
+        table = perm.view(w.B, npg).to(torch.int32)
+        us = _time_calls(lambda: m.attn_decode_mla_paged(qn, qr, lp, table, lens, w.scale, out, ws),
+                         stream, warmup, iters)
+        res["mla_paged64"] = {"workload": w.name + ", 64-position pages, permuted", "us": round(us, 2),
+                              "kv_GBps": round(it["kv"] / (us * 1e-6) / 1e9, 1)}
+        del lp
     return res
 
 

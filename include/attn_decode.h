@@ -165,6 +165,37 @@ int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_
                    const int32_t* seq_lens, int B, int h_kv, int D, int T_max, attn_dtype dt,
                    hipStream_t stream);
 
+/* Decode over a paged KV cache ("Attention variants: MQA, GQA, and MLA",
+ * section "Against the real libraries": serving engines keep the cache in
+ * fixed-size pages allocated like virtual memory and shared by sequences with
+ * a common prefix).
+ * k_pages, v_pages [num_pages, h_kv, page_size, D] dtype dt: page p holds
+ *                  page_size consecutive positions of every KV head;
+ * block_table      int32 [B, max_pages]: position t of sequence b lives in
+ *                  row t % page_size of page block_table[b, t / page_size].
+ * A sequence holds at most T_max = max_pages * page_size positions (seq_lens
+ * clamped to it); entries past a sequence's last used page are never read,
+ * and pages may be shared between sequences (read-only here). page_size: a
+ * power of two >= 16; the fast bf16 kernel (g <= 8) needs a multiple of 64,
+ * smaller pages go through a slower per-row gather. A used table entry outside
+ * [0, num_pages) never faults: its rows read as zeros (or as a clamped page on
+ * the per-row path) and the result for that sequence is unspecified.
+ * Workspace: attn_decode_gqa_workspace_bytes(B, h_q, h_kv, D, T_max, dt). */
+int attn_decode_gqa_paged(const void* q, const void* k_pages, const void* v_pages,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          int B, int h_q, int h_kv, int D, int num_pages, int page_size,
+                          int max_pages, float scale, attn_dtype dt, void* out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Append into a paged cache: k_new / v_new [B, h_kv, D] go to logical
+ * position pos = max(seq_lens[b], 0) (row pos % page_size of page
+ * block_table[b, pos / page_size]) unless pos >= T_max or that table entry is
+ * outside [0, num_pages); bit-exact copies. page_size: any power of two. */
+int attn_kv_append_paged(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                         const int32_t* block_table, const int32_t* seq_lens, int B, int h_kv,
+                         int D, int num_pages, int page_size, int max_pages, attn_dtype dt,
+                         hipStream_t stream);
+
 /* Stage 1 alone, with an explicit partition_size P >= 1 and NP = ceil(T_max / P):
  * part_out [B, h_q, NP, D] fp32: softmax-weighted average of V over the valid
  *          positions of partition p, i.e. t in [p*P, min((p+1)*P, n));
@@ -225,6 +256,23 @@ int attn_decode_mla_step(const void* q_nope_absorbed, const void* q_rope, const 
  * Any d_c + d_r that is a multiple of 8. */
 int attn_latent_append(const void* latent_new, void* latent_cache, const int32_t* seq_lens,
                        int B, int d_c, int d_r, int T_max, hipStream_t stream);
+
+/* Absorbed MLA over a paged latent cache (same page rules as
+ * attn_decode_gqa_paged): latent_pages [num_pages, page_size, d_c+d_r] bf16,
+ * block_table int32 [B, max_pages]; page_size a power of two >= 32 (one
+ * 32-position tile never spans two pages). Workspace:
+ * attn_decode_mla_workspace_bytes(B, H, d_c, d_r, max_pages * page_size). */
+int attn_decode_mla_paged(const void* q_nope_absorbed, const void* q_rope, const void* latent_pages,
+                          const int32_t* block_table, const int32_t* seq_lens, int B, int H,
+                          int d_c, int d_r, int num_pages, int page_size, int max_pages,
+                          float scale, void* out, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Append into a paged latent cache: latent_new [B, d_c+d_r] bf16 goes to
+ * logical position max(seq_lens[b], 0), same rules as attn_kv_append_paged. */
+int attn_latent_append_paged(const void* latent_new, void* latent_pages, const int32_t* block_table,
+                             const int32_t* seq_lens, int B, int d_c, int d_r, int num_pages,
+                             int page_size, int max_pages, hipStream_t stream);
 
 /* Stage 1 alone; same partial layout as attn_decode_gqa_partial with h_q = H
  * and D = d_c. Merge with attn_decode_merge(..., Dv = d_c, out_dt = ATTN_BF16). */

@@ -27,7 +27,8 @@ __all__ = [
     "attn_decode_mla_plan", "attn_decode_mla_workspace_bytes", "attn_decode_mla",
     "attn_decode_mla_partial",
     "attn_decode_gqa_step", "attn_kv_append", "attn_decode_mla_step", "attn_latent_append",
-    "attn_decode_gqa_window",
+    "attn_decode_gqa_window", "attn_decode_gqa_paged", "attn_kv_append_paged",
+    "attn_decode_mla_paged", "attn_latent_append_paged",
 ]
 
 
@@ -342,3 +343,98 @@ def attn_latent_append(latent_new, latent_cache, seq_lens, d_c: int = 512) -> No
     _check(load().attn_latent_append(_ptr(latent_new), _ptr(latent_cache), _ptr(seq_lens), B,
                                      int(d_c), W - int(d_c), T_max, _stream(dev)),
            "attn_latent_append")
+
+
+# ----------------------------------------------------------------------------- paged caches
+
+def _table(block_table, B):
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be int32 [{B}, max_pages]")
+    return block_table.shape[1]
+
+
+def attn_decode_gqa_paged(q, k_pages, v_pages, block_table, seq_lens, scale: Optional[float] = None,
+                          out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Decode over pages k_pages/v_pages [num_pages, h_kv, page_size, D]; block_table int32
+    [B, max_pages] maps sequence b's logical page i to a physical page. Returns out [B,h_q,D]."""
+    if q.dim() != 3 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
+        raise ValueError("expected q [B,h_q,D] and pages [num_pages,h_kv,page_size,D]")
+    B, h_q, D = q.shape
+    num_pages, h_kv, page_size, Dk = k_pages.shape
+    if Dk != D or not (q.dtype == k_pages.dtype == v_pages.dtype):
+        raise ValueError("q and the pages disagree on D or dtype")
+    dev = _dev(q, k_pages, v_pages, block_table, seq_lens)
+    _lens(seq_lens, B)
+    max_pages = _table(block_table, B)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    need = attn_decode_gqa_workspace_bytes(B, h_q, h_kv, D, max_pages * page_size, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(out, workspace)
+    _check(load().attn_decode_gqa_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                        _ptr(seq_lens), B, h_q, h_kv, D, num_pages, page_size,
+                                        max_pages, scale, _dt(q), _ptr(out), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(dev)),
+           "attn_decode_gqa_paged")
+    return out
+
+
+def attn_kv_append_paged(k_new, v_new, k_pages, v_pages, block_table, seq_lens) -> None:
+    """Write k_new/v_new [B,h_kv,D] at logical position seq_lens[b] of the paged caches (in place)."""
+    num_pages, h_kv, page_size, D = k_pages.shape
+    B = k_new.shape[0]
+    dev = _dev(k_new, v_new, k_pages, v_pages, block_table, seq_lens)
+    _lens(seq_lens, B)
+    max_pages = _table(block_table, B)
+    _new_rows(k_new, v_new, B, h_kv, D, k_pages.dtype)
+    _check(load().attn_kv_append_paged(_ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages),
+                                       _ptr(block_table), _ptr(seq_lens), B, h_kv, D, num_pages,
+                                       page_size, max_pages, _dt(k_pages), _stream(dev)),
+           "attn_kv_append_paged")
+
+
+def attn_decode_mla_paged(q_nope_absorbed, q_rope, latent_pages, block_table, seq_lens, scale: float,
+                          out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Absorbed MLA over latent pages [num_pages, page_size, d_c+d_r] bf16. Returns out [B,H,d_c]."""
+    if q_nope_absorbed.dim() != 3 or q_rope.dim() != 3 or latent_pages.dim() != 3:
+        raise ValueError("expected q_nope [B,H,d_c], q_rope [B,H,d_r], pages [num_pages,page_size,d_c+d_r]")
+    B, H, d_c = q_nope_absorbed.shape
+    d_r = q_rope.shape[2]
+    num_pages, page_size, W = latent_pages.shape
+    if W != d_c + d_r:
+        raise ValueError("latent page rows must be d_c + d_r wide")
+    for t in (q_nope_absorbed, q_rope, latent_pages):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("MLA inputs must be bfloat16")
+    dev = _dev(q_nope_absorbed, q_rope, latent_pages, block_table, seq_lens)
+    _lens(seq_lens, B)
+    max_pages = _table(block_table, B)
+    if out is None:
+        out = torch.empty((B, H, d_c), dtype=torch.bfloat16, device=dev)
+    need = attn_decode_mla_workspace_bytes(B, H, d_c, d_r, max_pages * page_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(out, workspace)
+    _check(load().attn_decode_mla_paged(_ptr(q_nope_absorbed), _ptr(q_rope), _ptr(latent_pages),
+                                        _ptr(block_table), _ptr(seq_lens), B, H, d_c, d_r, num_pages,
+                                        page_size, max_pages, float(scale), _ptr(out), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(dev)),
+           "attn_decode_mla_paged")
+    return out
+
+
+def attn_latent_append_paged(latent_new, latent_pages, block_table, seq_lens, d_c: int = 512) -> None:
+    """Write latent_new [B, d_c+d_r] at logical position seq_lens[b] of the latent pages (in place)."""
+    num_pages, page_size, W = latent_pages.shape
+    B = latent_new.shape[0]
+    dev = _dev(latent_new, latent_pages, block_table, seq_lens)
+    _lens(seq_lens, B)
+    max_pages = _table(block_table, B)
+    if tuple(latent_new.shape) != (B, W) or latent_new.dtype != torch.bfloat16:
+        raise ValueError(f"latent_new must be bfloat16 [{B}, {W}]")
+    _check(load().attn_latent_append_paged(_ptr(latent_new), _ptr(latent_pages), _ptr(block_table),
+                                           _ptr(seq_lens), B, int(d_c), W - int(d_c), num_pages,
+                                           page_size, max_pages, _stream(dev)),
+           "attn_latent_append_paged")

@@ -52,6 +52,11 @@ SIGNATURES = {
     "attn_latent_append": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp]),
     "attn_decode_gqa_window": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                         _c_int, _c_float, _c_int, _vp, _vp, _c_size, _vp]),
+    "attn_decode_gqa_paged": (_c_int, [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 7 +
+                              [_c_float, _c_int, _vp, _vp, _c_size, _vp]),
+    "attn_kv_append_paged": (_c_int, [_vp] * 6 + [_c_int] * 7 + [_vp]),
+    "attn_decode_mla_paged": (_c_int, [_vp] * 5 + [_c_int] * 7 + [_c_float, _vp, _vp, _c_size, _vp]),
+    "attn_latent_append_paged": (_c_int, [_vp] * 4 + [_c_int] * 6 + [_vp]),
 }
 
 _lock = threading.Lock()

@@ -22,9 +22,11 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Whether [a, a + na) and [b, b + nb) intersect; a null pointer (an argument
+// that is absent) overlaps nothing.
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return na && nb && x < y + nb && y < x + na;
+  return x && y && na && nb && x < y + nb && y < x + na;
 }
 
 int elem_size(attn_dtype dt) { return dt == ATTN_BF16 ? 2 : 4; }
@@ -138,6 +140,30 @@ int check_new_latent(const MlaShape& s, const void* lat_new, const void* qn, con
   return ATTN_OK;
 }
 
+// A paged cache as the kernels see it (block_table == nullptr: contiguous cache).
+struct Paged {
+  const int32_t* block_table = nullptr;
+  int page_size = 0, page_shift = 0, max_pages = 0, num_pages = 0;
+};
+
+int log2_exact(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return (1 << s) == x ? s : -1;
+}
+
+// Checks the page geometry; T_max of the paged cache is max_pages * page_size.
+int check_paged(const Paged& pg, int min_page, int* T_max) {
+  if (!pg.block_table) return ATTN_ERR_INVALID_ARG;
+  if (pg.page_size < 1 || pg.max_pages < 1 || pg.num_pages < 1) return ATTN_ERR_INVALID_ARG;
+  if (int64_t(pg.page_size) * pg.max_pages > kMaxTmax) return ATTN_ERR_INVALID_ARG;
+  if (log2_exact(pg.page_size) < 0 || pg.page_size < min_page || pg.page_size > (1 << 20))
+    return ATTN_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(pg.block_table) % 4 != 0) return ATTN_ERR_UNSUPPORTED;
+  *T_max = pg.page_size * pg.max_pages;
+  return ATTN_OK;
+}
+
 int set_plan(int P, int T_max, size_t ws, int* partition_size, int* num_partitions,
              size_t* workspace_bytes) {
   if (partition_size) *partition_size = P;
@@ -227,8 +253,9 @@ int attn_decode_gqa_partial(const void* q, const void* k_cache, const void* v_ca
   if (!part_lse) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(part_lse)) return ATTN_ERR_UNSUPPORTED;
   if (overlap(part_out, ob, part_lse, size_t(B) * h_q * NP * sizeof(float))) return ATTN_ERR_INVALID_ARG;
-  const attn::GqaArgs a{q, k_cache, v_cache, seq_lens, nullptr, nullptr, 0, B, h_kv, T_max,
-                        partition_size, NP, float(double(scale) * kLog2e), part_out, part_lse};
+  const attn::GqaArgs a{q, k_cache, v_cache, seq_lens, nullptr, nullptr, 0, nullptr, 0, 0, 0, 0,
+                        B, h_kv, T_max, partition_size, NP, float(double(scale) * kLog2e),
+                        part_out, part_lse};
   if (attn::launch_gqa_partial(int(dt), D, h_q / h_kv, a, stream) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -262,14 +289,32 @@ namespace {
 int gqa_decode_impl(const void* q, const void* k_new, const void* v_new, const void* k_cache,
                     const void* v_cache, const int32_t* seq_lens, int B, int h_q, int h_kv, int D,
                     int T_max, int window, float scale, attn_dtype dt, void* out, void* workspace,
-                    size_t workspace_bytes, hipStream_t stream) {
+                    size_t workspace_bytes, hipStream_t stream, const Paged& pg = Paged()) {
   const GqaShape s{B, h_q, h_kv, D, T_max, dt};
   int st = check_gqa_shape(s);
   if (st != ATTN_OK) return st;
   if (!isfinite(scale) || window < 0) return ATTN_ERR_INVALID_ARG;
   const size_t out_b = size_t(B) * h_q * D * elem_size(dt);
-  st = check_gqa_ptrs(s, q, k_cache, v_cache, seq_lens, out, out_b);
-  if (st != ATTN_OK) return st;
+  if (pg.block_table) {
+    // The caches are page arrays [num_pages, h_kv, page_size, D]: check them as
+    // one "sequence" of num_pages * page_size rows.
+    // Page arrays [num_pages, h_kv, page_size, D] are addressed with 64-bit
+    // offsets: only their total size is bounded.
+    if (int64_t(pg.num_pages) * h_kv * pg.page_size * D >= kMaxElems) return ATTN_ERR_INVALID_ARG;
+    if (!q || !k_cache || !v_cache || !seq_lens || !out) return ATTN_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+      return ATTN_ERR_UNSUPPORTED;
+    const size_t kb = size_t(pg.num_pages) * h_kv * pg.page_size * D * elem_size(dt);
+    if (overlap(out, out_b, k_cache, kb) || overlap(out, out_b, v_cache, kb)) return ATTN_ERR_INVALID_ARG;
+    const size_t tb = size_t(B) * pg.max_pages * 4;
+    if (overlap(out, out_b, q, size_t(B) * h_q * D * elem_size(dt)) ||
+        overlap(out, out_b, seq_lens, size_t(B) * 4) || overlap(out, out_b, pg.block_table, tb) ||
+        overlap(pg.block_table, tb, k_cache, kb) || overlap(pg.block_table, tb, v_cache, kb))
+      return ATTN_ERR_INVALID_ARG;
+  } else {
+    st = check_gqa_ptrs(s, q, k_cache, v_cache, seq_lens, out, out_b);
+    if (st != ATTN_OK) return st;
+  }
   // A window attends over at most `window` positions: plan for that span.
   const int span = window > 0 && window < T_max ? window : T_max;
   const GqaShape sp{B, h_q, h_kv, D, span, dt};
@@ -278,9 +323,11 @@ int gqa_decode_impl(const void* q, const void* k_new, const void* v_new, const v
   const size_t need = partial_bytes(int64_t(B) * h_q, NP, D);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
-  const size_t kb = size_t(B) * h_kv * size_t(T_max) * D * elem_size(dt);
+  const size_t kb = pg.block_table ? size_t(pg.num_pages) * h_kv * pg.page_size * D * elem_size(dt)
+                                   : size_t(B) * h_kv * size_t(T_max) * D * elem_size(dt);
   if (overlap(workspace, need, out, out_b) || overlap(workspace, need, k_cache, kb) ||
-      overlap(workspace, need, v_cache, kb))
+      overlap(workspace, need, v_cache, kb) ||
+      overlap(workspace, need, pg.block_table, size_t(B) * pg.max_pages * 4))
     return ATTN_ERR_INVALID_ARG;
   if (k_new) {
     st = check_new_rows(s, k_new, v_new, q, k_cache, v_cache, seq_lens, out, out_b, workspace, need);
@@ -289,8 +336,9 @@ int gqa_decode_impl(const void* q, const void* k_new, const void* v_new, const v
   float* part_out = static_cast<float*>(workspace);
   float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                              align_up(size_t(B) * h_q * NP * D * sizeof(float)));
-  const attn::GqaArgs a{q, k_cache, v_cache, seq_lens, k_new, v_new, window, B, h_kv, T_max, P,
-                        NP, float(double(scale) * kLog2e), part_out, part_lse};
+  const attn::GqaArgs a{q, k_cache, v_cache, seq_lens, k_new, v_new, window, pg.block_table,
+                        pg.page_size, pg.page_shift, pg.max_pages, pg.num_pages, B, h_kv, T_max,
+                        P, NP, float(double(scale) * kLog2e), part_out, part_lse};
   if (attn::launch_gqa_partial(int(dt), D, h_q / h_kv, a, stream) != hipSuccess) return ATTN_ERR_HIP;
   if (attn::launch_merge(int(dt), part_out, part_lse, seq_lens, k_new ? 1 : 0, window, B, h_q, D,
                          T_max, P, NP, out, stream) != hipSuccess)
@@ -345,6 +393,57 @@ int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_
   return ATTN_OK;
 }
 
+int attn_decode_gqa_paged(const void* q, const void* k_pages, const void* v_pages,
+                          const int32_t* block_table, const int32_t* seq_lens, int B, int h_q,
+                          int h_kv, int D, int num_pages, int page_size, int max_pages, float scale,
+                          attn_dtype dt, void* out, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  Paged pg;
+  pg.block_table = block_table;
+  pg.page_size = page_size;
+  pg.page_shift = log2_exact(page_size);
+  pg.max_pages = max_pages;
+  pg.num_pages = num_pages;
+  int T_max = 0;
+  const int st = check_paged(pg, 16, &T_max);
+  if (st != ATTN_OK) return st;
+  return gqa_decode_impl(q, nullptr, nullptr, k_pages, v_pages, seq_lens, B, h_q, h_kv, D, T_max, 0,
+                         scale, dt, out, workspace, workspace_bytes, stream, pg);
+}
+
+int attn_kv_append_paged(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                         const int32_t* block_table, const int32_t* seq_lens, int B, int h_kv, int D,
+                         int num_pages, int page_size, int max_pages, attn_dtype dt,
+                         hipStream_t stream) {
+  Paged pg;
+  pg.block_table = block_table;
+  pg.page_size = page_size;
+  pg.max_pages = max_pages;
+  pg.num_pages = num_pages;
+  int T_max = 0;
+  int st = check_paged(pg, 1, &T_max);
+  if (st != ATTN_OK) return st;
+  const GqaShape ps{num_pages, h_kv, h_kv, D, page_size, dt};
+  st = check_gqa_shape(ps);
+  if (st != ATTN_OK) return st;
+  if (B < 1 || B > kMaxGridYZ || !seq_lens || !k_pages || !v_pages) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(k_pages) || !aligned16(v_pages)) return ATTN_ERR_UNSUPPORTED;
+  const GqaShape rows{B, h_kv, h_kv, D, 1, dt};
+  st = check_new_rows(rows, k_new, v_new, nullptr, nullptr, nullptr, seq_lens, nullptr, 0, nullptr, 0);
+  if (st != ATTN_OK) return st;
+  const size_t es = elem_size(dt), nb = size_t(B) * h_kv * D * es;
+  const size_t kb = size_t(num_pages) * h_kv * page_size * D * es, tb = size_t(B) * max_pages * 4;
+  for (const void* x : {k_new, v_new, static_cast<const void*>(block_table), static_cast<const void*>(seq_lens)}) {
+    const size_t xb = x == block_table ? tb : (x == seq_lens ? size_t(B) * 4 : nb);
+    if (overlap(x, xb, k_pages, kb) || overlap(x, xb, v_pages, kb)) return ATTN_ERR_INVALID_ARG;
+  }
+  if (overlap(k_pages, kb, v_pages, kb)) return ATTN_ERR_INVALID_ARG;
+  if (attn::launch_append_paged(k_new, v_new, k_pages, v_pages, block_table, seq_lens, B, h_kv,
+                                int(D * es), page_size, max_pages, num_pages, stream) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
 // ------------------------------------------------------------------ MLA
 
 int attn_decode_mla_plan(int B, int H, int d_c, int d_r, int T_max, int* partition_size,
@@ -392,8 +491,8 @@ int attn_decode_mla_partial(const void* q_nope, const void* q_rope, const void* 
   if (!part_lse) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(part_lse)) return ATTN_ERR_UNSUPPORTED;
   if (overlap(part_out, ob, part_lse, size_t(B) * H * NP * sizeof(float))) return ATTN_ERR_INVALID_ARG;
-  const attn::MlaArgs a{q_nope, q_rope, latent, seq_lens, nullptr, B, H, T_max, partition_size, NP,
-                        float(double(scale) * kLog2e), part_out, part_lse};
+  const attn::MlaArgs a{q_nope, q_rope, latent, seq_lens, nullptr, nullptr, 0, 0, 0, 0, B, H, T_max,
+                        partition_size, NP, float(double(scale) * kLog2e), part_out, part_lse};
   if (attn::launch_mla_partial(a, stream) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -405,21 +504,37 @@ namespace {
 int mla_decode_impl(const void* q_nope, const void* q_rope, const void* lat_new,
                     const void* latent, const int32_t* seq_lens, int B, int H, int d_c, int d_r,
                     int T_max, float scale, void* out, void* workspace, size_t workspace_bytes,
-                    hipStream_t stream) {
+                    hipStream_t stream, const Paged& pg = Paged()) {
   const MlaShape s{B, H, d_c, d_r, T_max};
   int st = check_mla_shape(s);
   if (st != ATTN_OK) return st;
   if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
   const size_t out_b = size_t(B) * H * d_c * 2;
-  st = check_mla_ptrs(s, q_nope, q_rope, latent, seq_lens, out, out_b);
-  if (st != ATTN_OK) return st;
+  if (pg.block_table) {
+    if (int64_t(pg.num_pages) * pg.page_size * (d_c + d_r) >= kMaxElems) return ATTN_ERR_INVALID_ARG;
+    const MlaShape ps{1, H, d_c, d_r, pg.num_pages * pg.page_size};
+    st = check_mla_ptrs(ps, q_nope, q_rope, latent, seq_lens, out, out_b);
+    if (st != ATTN_OK) return st;
+    const size_t lb = size_t(pg.num_pages) * pg.page_size * (d_c + d_r) * 2;
+    const size_t tb = size_t(B) * pg.max_pages * 4;
+    const size_t qnb = size_t(B) * H * d_c * 2, qrb = size_t(B) * H * d_r * 2;
+    if (overlap(out, out_b, q_nope, qnb) || overlap(out, out_b, q_rope, qrb) ||
+        overlap(out, out_b, seq_lens, size_t(B) * 4) || overlap(out, out_b, pg.block_table, tb) ||
+        overlap(pg.block_table, tb, latent, lb))
+      return ATTN_ERR_INVALID_ARG;
+  } else {
+    st = check_mla_ptrs(s, q_nope, q_rope, latent, seq_lens, out, out_b);
+    if (st != ATTN_OK) return st;
+  }
   const int P = mla_auto_partition(s);
   const int NP = ceil_div(T_max, P);
   const size_t need = partial_bytes(int64_t(B) * H, NP, d_c);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
-  const size_t lb = size_t(B) * size_t(T_max) * (d_c + d_r) * 2;
-  if (overlap(workspace, need, out, out_b) || overlap(workspace, need, latent, lb))
+  const size_t lb = pg.block_table ? size_t(pg.num_pages) * pg.page_size * (d_c + d_r) * 2
+                                   : size_t(B) * size_t(T_max) * (d_c + d_r) * 2;
+  if (overlap(workspace, need, out, out_b) || overlap(workspace, need, latent, lb) ||
+      overlap(workspace, need, pg.block_table, size_t(B) * pg.max_pages * 4))
     return ATTN_ERR_INVALID_ARG;
   if (lat_new) {
     st = check_new_latent(s, lat_new, q_nope, q_rope, latent, seq_lens, out, out_b, workspace, need);
@@ -428,7 +543,8 @@ int mla_decode_impl(const void* q_nope, const void* q_rope, const void* lat_new,
   float* part_out = static_cast<float*>(workspace);
   float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                              align_up(size_t(B) * H * NP * d_c * sizeof(float)));
-  const attn::MlaArgs a{q_nope, q_rope, latent, seq_lens, lat_new, B, H, T_max, P, NP,
+  const attn::MlaArgs a{q_nope, q_rope, latent, seq_lens, lat_new, pg.block_table, pg.page_size,
+                        pg.page_shift, pg.max_pages, pg.num_pages, B, H, T_max, P, NP,
                         float(double(scale) * kLog2e), part_out, part_lse};
   if (attn::launch_mla_partial(a, stream) != hipSuccess) return ATTN_ERR_HIP;
   if (attn::launch_merge(int(ATTN_BF16), part_out, part_lse, seq_lens, lat_new ? 1 : 0, 0, B, H,
@@ -456,6 +572,50 @@ int attn_decode_mla_step(const void* q_nope, const void* q_rope, const void* lat
   if (!latent_new) return ATTN_ERR_INVALID_ARG;
   return mla_decode_impl(q_nope, q_rope, latent_new, latent_cache, seq_lens, B, H, d_c, d_r, T_max,
                          scale, out, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_mla_paged(const void* q_nope, const void* q_rope, const void* latent_pages,
+                          const int32_t* block_table, const int32_t* seq_lens, int B, int H, int d_c,
+                          int d_r, int num_pages, int page_size, int max_pages, float scale, void* out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Paged pg;
+  pg.block_table = block_table;
+  pg.page_size = page_size;
+  pg.page_shift = log2_exact(page_size);
+  pg.max_pages = max_pages;
+  pg.num_pages = num_pages;
+  int T_max = 0;
+  const int st = check_paged(pg, 32, &T_max);
+  if (st != ATTN_OK) return st;
+  return mla_decode_impl(q_nope, q_rope, nullptr, latent_pages, seq_lens, B, H, d_c, d_r, T_max,
+                         scale, out, workspace, workspace_bytes, stream, pg);
+}
+
+int attn_latent_append_paged(const void* latent_new, void* latent_pages, const int32_t* block_table,
+                             const int32_t* seq_lens, int B, int d_c, int d_r, int num_pages,
+                             int page_size, int max_pages, hipStream_t stream) {
+  Paged pg;
+  pg.block_table = block_table;
+  pg.page_size = page_size;
+  pg.max_pages = max_pages;
+  pg.num_pages = num_pages;
+  int T_max = 0;
+  const int st = check_paged(pg, 1, &T_max);
+  if (st != ATTN_OK) return st;
+  if (B < 1 || B > kMaxGridYZ || d_c < 1 || d_r < 0 || !latent_new || !latent_pages || !seq_lens)
+    return ATTN_ERR_INVALID_ARG;
+  if (int64_t(num_pages) * page_size * (d_c + d_r) >= kMaxElems) return ATTN_ERR_INVALID_ARG;
+  if ((d_c + d_r) % 8 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(latent_new) || !aligned16(latent_pages)) return ATTN_ERR_UNSUPPORTED;
+  const size_t row = size_t(d_c + d_r) * 2, nb = size_t(B) * row;
+  const size_t lb = size_t(num_pages) * page_size * row, tb = size_t(B) * max_pages * 4;
+  if (overlap(latent_new, nb, latent_pages, lb) || overlap(block_table, tb, latent_pages, lb) ||
+      overlap(seq_lens, size_t(B) * 4, latent_pages, lb))
+    return ATTN_ERR_INVALID_ARG;
+  if (attn::launch_append_paged(latent_new, nullptr, latent_pages, nullptr, block_table, seq_lens, B,
+                                1, int(row), page_size, max_pages, num_pages, stream) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
 }
 
 int attn_latent_append(const void* latent_new, void* latent_cache, const int32_t* seq_lens, int B,

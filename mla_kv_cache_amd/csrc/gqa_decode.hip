@@ -121,16 +121,31 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const GqaArgs a) 
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
 
-  const size_t head_off = ((size_t)b * h_kv + j) * (size_t)T_max * D + (size_t)c * EPL;
+  const bool paged = a.block_table != nullptr;
+  const size_t head_off = paged ? (size_t)j * a.page_size * D + (size_t)c * EPL
+                                : ((size_t)b * h_kv + j) * (size_t)T_max * D + (size_t)c * EPL;
   const typename E::storage* kb = kc + head_off;
   const typename E::storage* vb = vc + head_off;
+  // Element offset of row r (clamped to the partition) from kb / vb. Paged:
+  // page lookup per row; a table entry outside [0, num_pages) is clamped
+  // into range (the row's values are then unspecified, never a fault).
+  const int32_t* bt = paged ? a.block_table + (size_t)b * a.max_pages : nullptr;
+  auto row_off = [&](int r) -> size_t {
+    r = min(r, end - 1);
+    if (!paged) return (size_t)r * D;
+    const int phys = min(max(bt[r >> a.page_shift], 0), a.num_pages - 1);
+    return (((size_t)phys * h_kv) * a.page_size + (r & (a.page_size - 1))) * D;
+  };
 
   for (int r0 = start + wave * RB; r0 < end; r0 += kWaves * RB) {
     uint4 kr[NI], vr[NI];
+    size_t ro[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kr[i] = ld16(kb + (size_t)min(r0 + i * RPI + rr, end - 1) * D);
+    for (int i = 0; i < NI; ++i) ro[i] = row_off(r0 + i * RPI + rr);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) vr[i] = ld16(vb + (size_t)min(r0 + i * RPI + rr, end - 1) * D);
+    for (int i = 0; i < NI; ++i) kr[i] = ld16(kb + ro[i]);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) vr[i] = ld16(vb + ro[i]);
 
     float s[NI][G];
 #pragma unroll
@@ -580,12 +595,32 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
   // sequence's valid rows: a read at or past row n returns zeros, so the
   // tail of the last tile needs no clamping and padding rows are never
   // fetched. Byte offsets fit 32 bits (the host limits T_max * D * 2).
-  const size_t head_off = ((size_t)b * h_kv + j) * (size_t)T_max * D;
+  // A paged cache gets one pair of resources per tile instead (tile_rsrc).
+  const bool paged = a.block_table != nullptr;
+  const size_t head_off = paged ? 0 : ((size_t)b * h_kv + j) * (size_t)T_max * D;
   const int valid_bytes = n * (D * 2);
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + head_off), 0, valid_bytes, kBufWord3);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + head_off), 0, valid_bytes, kBufWord3);
+  // Paged: the 64 rows of a tile lie in one page (page_size is a multiple of
+  // 64 and tiles start at multiples of 64); its resources cover the tile's
+  // rows below n, and a table entry outside [0, num_pages) reads as zeros.
+  auto tile_rsrc = [&](int t0, __amdgpu_buffer_rsrc_t& kr, __amdgpu_buffer_rsrc_t& vr_, uint32_t& toff) {
+    if (!paged) {
+      kr = krs;
+      vr_ = vrs;
+      toff = (uint32_t)t0 * (D * 2);
+      return;
+    }
+    const int phys = a.block_table[(size_t)b * a.max_pages + (t0 >> a.page_shift)];
+    const bool ok = phys >= 0 && phys < a.num_pages;
+    const int rows = ok ? min(kPoRows, n - t0) : 0;
+    const size_t off = (((size_t)(ok ? phys : 0) * h_kv + j) * a.page_size + (t0 & (a.page_size - 1))) * D;
+    kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + off), 0, rows * (D * 2), kBufWord3);
+    vr_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + off), 0, rows * (D * 2), kBufWord3);
+    toff = 0;
+  };
   const uint32_t kt_lds = __builtin_amdgcn_readfirstlane(lds_addr(&ktile[wave][0]));
   const unsigned char* kt = &ktile[wave][0];
   float* wt = &wtab[wave][0][0];
@@ -603,28 +638,30 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
     const int lc = pc ^ ((RPC * mm + rl) % CH);
     kvoff[mm] = (uint32_t)(rl * D + lc * 8) * 2u;
   }
-  auto copy_k = [&](int t0) {
-    const uint32_t tile_off = (uint32_t)t0 * (D * 2);
+  auto copy_k = [&](const __amdgpu_buffer_rsrc_t& kr, uint32_t tile_off) {
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       const uint32_t soff = tile_off + 1024u * i;
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                   ::"s"(kt_lds + 1024u * i), "v"(kvoff[i % KPER]), "s"(krs), "s"(soff)
+                   ::"s"(kt_lds + 1024u * i), "v"(kvoff[i % KPER]), "s"(kr), "s"(soff)
                    : "memory");
     }
   };
   // V rows -> registers (row layout): load i brings rows i*RPI .. i*RPI+RPI-1.
   const uint32_t vvoff = (uint32_t)(rr * D + c * 8) * 2u;
-  auto load_v = [&](int t0, int i) {
-    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(vrs, vvoff, (uint32_t)t0 * (D * 2) + 1024u * i, 0);
+  auto load_v = [&](const __amdgpu_buffer_rsrc_t& vr_, uint32_t tile_off, int i) {
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(vr_, vvoff, tile_off + 1024u * i, 0);
     return make_uint4(w.x, w.y, w.z, w.w);
   };
 
   for (int t0 = start + wave * kPoRows; t0 < end; t0 += kWaves * kPoRows) {
-    copy_k(t0);
+    __amdgpu_buffer_rsrc_t krt, vrt;
+    uint32_t toff;
+    tile_rsrc(t0, krt, vrt, toff);
+    copy_k(krt, toff);
     uint4 vr[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) vr[i] = load_v(t0, i);
+    for (int i = 0; i < NV; ++i) vr[i] = load_v(vrt, toff, i);
     // The K copies were issued first: once at most NV memory operations of
     // this wave are outstanding, they have all landed.
     if constexpr (NV == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
@@ -810,7 +847,9 @@ constexpr int kPoMinGroup = ATTN_PO_MIN_GROUP;
 template <class E, int D>
 hipError_t launch_d(int G, const GqaArgs& a, hipStream_t s) {
   if constexpr (sizeof(typename E::storage) == 2) {
-    if (G >= kPoMinGroup) {
+    // The position-per-lane kernel reads a paged cache one 64-row tile at a time.
+    const bool tiles_fit = a.block_table == nullptr || a.page_size % kPoRows == 0;
+    if (G >= kPoMinGroup && tiles_fit) {
       switch (G) {
         case 1: return launch_po<D, 1>(a, s);
         case 2: return launch_po<D, 2>(a, s);
@@ -869,6 +908,48 @@ hipError_t launch_gqa_partial(int dt, int D, int group, const GqaArgs& a, hipStr
     if (D == 64) return launch_d<F32Elem, 64>(group, a, s);
   }
   return hipErrorInvalidValue;
+}
+
+namespace {
+
+// One thread per 16-byte piece of a new row: piece i of row (b, head) goes to
+// row pos % page_size of page block_table[b][pos / page_size] (and of the
+// second page array, when there is one).
+__global__ __launch_bounds__(256) void append_paged_kernel(
+    const unsigned char* __restrict__ new_a, const unsigned char* __restrict__ new_b,
+    unsigned char* __restrict__ pages_a, unsigned char* __restrict__ pages_b,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int B, int heads,
+    int row_pieces, int page_size, int max_pages, int num_pages) {
+  const int64_t total = (int64_t)B * heads * row_pieces;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t bh = t / row_pieces;
+    const int piece = (int)(t % row_pieces);
+    const int b = (int)(bh / heads), h = (int)(bh % heads);
+    const int pos = max(seq_lens[b], 0);
+    if (pos >= max_pages * page_size) continue;
+    const int phys = block_table[(size_t)b * max_pages + pos / page_size];
+    if (phys < 0 || phys >= num_pages) continue;
+    const size_t dst = ((((size_t)phys * heads + h) * page_size + pos % page_size) * row_pieces + piece) * 16;
+    st16(pages_a + dst, ld16(new_a + (size_t)t * 16));
+    if (pages_b) st16(pages_b + dst, ld16(new_b + (size_t)t * 16));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append_paged(const void* new_a, const void* new_b, void* pages_a, void* pages_b,
+                               const int32_t* block_table, const int32_t* seq_lens, int B,
+                               int heads, int row_bytes, int page_size, int max_pages,
+                               int num_pages, hipStream_t s) {
+  const int row_pieces = row_bytes / 16;
+  const int64_t total = (int64_t)B * heads * row_pieces;
+  const int blocks = (int)std::min<int64_t>((total + 255) / 256, 4096);
+  hipLaunchKernelGGL(append_paged_kernel, dim3(blocks), dim3(256), 0, s,
+                     static_cast<const unsigned char*>(new_a), static_cast<const unsigned char*>(new_b),
+                     static_cast<unsigned char*>(pages_a), static_cast<unsigned char*>(pages_b),
+                     block_table, seq_lens, B, heads, row_pieces, page_size, max_pages, num_pages);
+  return hipGetLastError();
 }
 
 hipError_t launch_kv_append(int dt, const void* k_new, const void* v_new, void* k, void* v,

@@ -19,6 +19,11 @@ struct GqaArgs {
   const void* k_new;          // decode step: [B, h_kv, D] rows appended at seq_lens[b]
   const void* v_new;          //   before attending; nullptr: plain decode
   int window;                 // > 0: attend over [max(0, n - window), n) only; 0: all of [0, n)
+  // Paged cache (block_table != nullptr): k and v are [num_pages, h_kv, page_size, D] and
+  // position t of sequence b is row t % page_size of page block_table[b * max_pages + t / page_size];
+  // T_max = max_pages * page_size. page_size is a power of two.
+  const int32_t* block_table;
+  int page_size, page_shift, max_pages, num_pages;
   int B, h_kv, T_max, P, NP;
   float qk_scale_log2;        // scale * log2(e)
   float* part_out;            // [B, h_q, NP, D]
@@ -49,6 +54,11 @@ struct MlaArgs {
   const void* latent;         // [B, T_max, 576]; written only in a decode step
   const int32_t* seq_lens;    // [B]
   const void* lat_new;        // decode step: [B, 576] rows appended at seq_lens[b]; nullptr: plain decode
+  // Paged cache (block_table != nullptr): latent is [num_pages, page_size, 576], page_size a
+  // power of two >= 32; position t of sequence b is row t % page_size of page
+  // block_table[b * max_pages + t / page_size]; T_max = max_pages * page_size.
+  const int32_t* block_table;
+  int page_size, page_shift, max_pages, num_pages;
   int B, H, T_max, P, NP;
   float qk_scale_log2;
   float* part_out;            // [B, H, NP, 512]
@@ -59,5 +69,14 @@ hipError_t launch_mla_partial(const MlaArgs& a, hipStream_t stream);
 
 hipError_t launch_latent_append(const void* lat_new, void* latent, const int32_t* seq_lens,
                                 int B, int row_elems, int T_max, hipStream_t stream);
+
+// Paged forms of the appends: the new row of sequence b goes to row pos % page_size of
+// page block_table[b * max_pages + pos / page_size], pos = max(seq_lens[b], 0), unless
+// pos >= max_pages * page_size or that table entry lies outside [0, num_pages).
+// rows_per_page_row: h_kv for KV pages ([num_pages, h_kv, page_size, row]), 1 for latent pages.
+hipError_t launch_append_paged(const void* new_a, const void* new_b, void* pages_a, void* pages_b,
+                               const int32_t* block_table, const int32_t* seq_lens, int B,
+                               int heads, int row_bytes, int page_size, int max_pages,
+                               int num_pages, hipStream_t stream);
 
 }  // namespace attn

@@ -109,9 +109,13 @@ constexpr int kHalfTiles = kOTiles / 2;                  // 8 output tiles per w
 // wait for the copy before every later LDS read (it cannot prove that the
 // reads touch the other buffer); the kernel waits for the copy itself
 // (s_waitcnt vmcnt(0) before the barrier that opens the next tile).
+// Row r of the tile is read at base + (r - base_row) * 576: for a contiguous
+// cache base is the sequence's first row and base_row = 0; for a paged cache
+// base is the page row that holds t0, base_row = t0 (the tile lies inside one
+// page).
 template <int NWAVES>
-__device__ __forceinline__ void copy_tile(unsigned char* buf, const uint16_t* lat_b, int t0, int end,
-                                          int wave, int lane) {
+__device__ __forceinline__ void copy_tile(unsigned char* buf, const uint16_t* base, int base_row, int t0,
+                                          int end, int wave, int lane) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)buf;
 #pragma unroll
   for (int k = 0; k < TileCopy<NWAVES>::kPerWave; ++k) {
@@ -120,7 +124,7 @@ __device__ __forceinline__ void copy_tile(unsigned char* buf, const uint16_t* la
     const int row = ci / kRowChunks, c16 = ci % kRowChunks;
     const bool data = row < kTile && c16 < kRow / 8;
     const int grow = min(t0 + (data ? row : 0), end - 1);
-    const uint16_t* src = lat_b + (size_t)grow * kRow + (data ? c16 * 8 : 0);
+    const uint16_t* src = base + (size_t)(grow - base_row) * kRow + (data ? c16 * 8 : 0);
     const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + 1024u * (uint32_t)blk);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "memory");
   }
@@ -143,7 +147,7 @@ __device__ __forceinline__ void wait_tile_barrier(bool next_in_flight) {
   }
 }
 
-template <int NHB>
+template <int NHB, bool PAGED>
 __global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(const MlaArgs a) {
   const uint16_t* __restrict__ q_nope = static_cast<const uint16_t*>(a.q_nope);
   const uint16_t* __restrict__ q_rope = static_cast<const uint16_t*>(a.q_rope);
@@ -201,7 +205,19 @@ __global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(const MlaArgs
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
   float m = kNegInf, lsum = 0.f;
 
-  const uint16_t* lat_b = lat + (size_t)b * T_max * kRow;
+  const uint16_t* lat_b = lat + (PAGED ? 0 : (size_t)b * T_max * kRow);
+  // Paged: the page row that holds row t0 (page_size is a multiple of the
+  // tile, tiles start at multiples of it); a table entry outside
+  // [0, num_pages) is clamped into range (values unspecified, never a fault).
+  auto page_base = [&](int t0) -> const uint16_t* {
+    const int phys = min(max(a.block_table[(size_t)b * a.max_pages + (t0 >> a.page_shift)], 0),
+                         a.num_pages - 1);
+    return lat + ((size_t)phys * a.page_size + (t0 & (a.page_size - 1))) * kRow;
+  };
+  auto copy = [&](unsigned char* buf, int t0) {
+    if constexpr (PAGED) copy_tile<NWAVES>(buf, page_base(t0), t0, t0, end, wave, lane);
+    else copy_tile<NWAVES>(buf, lat_b, 0, t0, end, wave, lane);
+  };
   // LDS transpose-read addressing, constant per lane (see the file comment).
   const int g16 = lane >> 4, i16 = lane & 15;
   const int tr_row = 4 * (g16 >> 1) + (i16 >> 2);
@@ -212,7 +228,7 @@ __global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(const MlaArgs
   auto tile = [&](const unsigned char* __restrict__ cur_b, unsigned char* __restrict__ nxt_b, int t0) {
     const uint16_t* cur = reinterpret_cast<const uint16_t*>(cur_b);
     wait_tile_barrier<TC::kPerWave>(t0 + kTile < end);
-    if (t0 + 2 * kTile < end) copy_tile<NWAVES>(nxt_b, lat_b, t0 + 2 * kTile, end, wave, lane);
+    if (t0 + 2 * kTile < end) copy(nxt_b, t0 + 2 * kTile);
 
     // ---- partial scores over this wave's 288 dims: S^T = L . Q^T
     f32x16 s;
@@ -308,8 +324,8 @@ __global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(const MlaArgs
     }
   };
 
-  copy_tile<NWAVES>(buf0, lat_b, start, end, wave, lane);
-  if (start + kTile < end) copy_tile<NWAVES>(buf1, lat_b, start + kTile, end, wave, lane);
+  copy(buf0, start);
+  if (start + kTile < end) copy(buf1, start + kTile);
   for (int t0 = start;;) {
     tile(buf0, buf2, t0);
     if ((t0 += kTile) >= end) break;
@@ -342,16 +358,21 @@ bool mla_supported(int H, int d_c, int d_r) {
   return d_c == kDc && d_r == kDr && H >= 32 && H % 32 == 0 && (H <= 128 || H % 128 == 0);
 }
 
-hipError_t launch_mla_partial(const MlaArgs& a, hipStream_t stream) {
+template <bool PAGED>
+hipError_t launch_mla_nhb(const MlaArgs& a, hipStream_t stream) {
   const int nhb = a.H >= 128 ? 4 : a.H / 32;  // 32-head blocks per work-group
   const dim3 grid(a.NP, a.H / (32 * nhb), a.B);
   switch (nhb) {
-    case 4: hipLaunchKernelGGL(mla_partial_kernel<4>, grid, dim3(512), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(mla_partial_kernel<3>, grid, dim3(384), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(mla_partial_kernel<2>, grid, dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL(mla_partial_kernel<1>, grid, dim3(128), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((mla_partial_kernel<4, PAGED>), grid, dim3(512), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((mla_partial_kernel<3, PAGED>), grid, dim3(384), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((mla_partial_kernel<2, PAGED>), grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((mla_partial_kernel<1, PAGED>), grid, dim3(128), 0, stream, a); break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_mla_partial(const MlaArgs& a, hipStream_t stream) {
+  return a.block_table ? launch_mla_nhb<true>(a, stream) : launch_mla_nhb<false>(a, stream);
 }
 
 namespace {

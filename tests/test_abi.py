@@ -232,3 +232,34 @@ def test_window_argument_checks(lib):
     need = lib.attn_decode_gqa_workspace_bytes(2, 8, 2, 128, 64, BF16)
     assert 0 < need < lib.attn_decode_gqa_workspace_bytes(2, 8, 2, 128, 1024, BF16)
     assert f(*base, 64, 0.1, BF16, OUT, WS, need - 1, None) == WORKSPACE
+
+
+def test_paged_argument_checks(lib):
+    f = lib.attn_decode_gqa_paged
+    BT = ctypes.c_void_p(1 << 45)
+
+    def call(**kw):
+        a = dict(q=P16, k=P16b, v=P16c, bt=BT, lens=LENS, B=2, h_q=8, h_kv=2, D=128, num_pages=64,
+                 ps=64, maxp=16, scale=0.1, dt=BF16, out=OUT, ws=WS, wsb=1 << 30)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["B"], a["h_q"], a["h_kv"], a["D"],
+                 a["num_pages"], a["ps"], a["maxp"], a["scale"], a["dt"], a["out"], a["ws"], a["wsb"], None)
+
+    assert call(bt=NULL) == INVALID
+    assert call(ps=48) == UNSUPPORTED            # not a power of two
+    assert call(ps=8) == UNSUPPORTED             # below the smallest page
+    assert call(maxp=0) == INVALID
+    assert call(num_pages=0) == INVALID
+    assert call(bt=ctypes.c_void_p((1 << 45) + 2)) == UNSUPPORTED
+    assert call(out=P16b) == INVALID             # output inside the K pages
+    assert call(wsb=16) == WORKSPACE
+    m = lib.attn_decode_mla_paged
+    assert m(P16, P16b, P16c, BT, LENS, 4, 128, 512, 64, 64, 16, 16, 0.07, OUT, WS, 1 << 30, None) == UNSUPPORTED
+    assert m(P16, P16b, P16c, NULL, LENS, 4, 128, 512, 64, 64, 64, 16, 0.07, OUT, WS, 1 << 30, None) == INVALID
+    ap = lib.attn_kv_append_paged
+    KN, VN = ctypes.c_void_p(1 << 46), ctypes.c_void_p(1 << 47)
+    assert ap(KN, VN, P16b, P16c, NULL, LENS, 2, 2, 128, 64, 64, 16, BF16, None) == INVALID
+    assert ap(KN, VN, P16b, P16b, BT, LENS, 2, 2, 128, 64, 64, 16, BF16, None) == INVALID
+    la = lib.attn_latent_append_paged
+    assert la(KN, P16c, BT, LENS, 4, 512, 60, 64, 64, 16, None) == UNSUPPORTED
+

@@ -24,6 +24,8 @@ float64 on the exact input values (bf16 inputs are widened exactly):
 * ``paged.decode_gqa_paged`` / ``paged.decode_mla_paged`` -- decode over a
   paged cache whose block table maps logical pages to physical ones
   (``paged.append_kv_paged`` writes one new row into its page).
+* ``absorb.absorb_q`` / ``absorb.up_v`` -- the MLA key up-projection absorbed
+  into the query before the decode, and the value up-projection after it.
 * ``cache.kv_cache_bytes`` / ``cache.mla_cache_bytes`` -- the cache-size
   arithmetic.
 * ``brute`` -- pure-Python scalar loops for tiny shapes (a second,
@@ -45,5 +47,6 @@ from .attention import (  # noqa: F401
 from .step import append_kv, append_latent, decode_gqa_step, decode_mla_step  # noqa: F401
 from .window import decode_gqa_window, window_start  # noqa: F401
 from .paged import decode_gqa_paged, decode_mla_paged, append_kv_paged  # noqa: F401
+from .absorb import absorb_q, up_v  # noqa: F401
 from .cache import kv_cache_bytes, mla_cache_bytes  # noqa: F401
 from . import brute  # noqa: F401

@@ -180,8 +180,9 @@ def _time_calls(fn, stream, warmup, iters):
 
 def time_next_rows(m, W, dev, stream, items, warmup, iters):
     """Time the rows built beside the decode path, on the bench's own inputs (not in `value`):
-    the decode step that appends the new row (GQA g=8, MLA), sliding-window decode and the
-    paged cache (the same caches in 64-position pages at permuted physical slots)."""
+    the decode step that appends the new row (GQA g=8, MLA), sliding-window decode, the
+    paged cache (the same caches in 64-position pages at permuted physical slots) and the
+    MLA absorption products around the decode."""
     import torch
     res = {}
     by = {it["name"]: it for it in items}
@@ -248,6 +249,24 @@ def time_next_rows(m, W, dev, stream, items, warmup, iters):
         res["mla_paged64"] = {"workload": w.name + ", 64-position pages, permuted", "us": round(us, 2),
                               "kv_GBps": round(it["kv"] / (us * 1e-6) / 1e9, 1)}
         del lp
+        # the absorption products around the decode: W_UK and W_UV of [H, d_c, 128], page init scale
+        d_h = d_v = 128
+        g = torch.Generator().manual_seed(2)
+        qh = torch.randn((w.B, w.H, d_h), generator=g).to(torch.bfloat16).to(dev)
+        w_uk = (torch.randn((w.H, w.d_c, d_h), generator=g) / w.d_c ** 0.5).to(torch.bfloat16).to(dev)
+        w_uv = (torch.randn((w.H, w.d_c, d_v), generator=g) / w.d_c ** 0.5).to(torch.bfloat16).to(dev)
+        q_lat = torch.empty((w.B, w.H, w.d_c), dtype=torch.bfloat16, device=dev)
+        o = torch.empty((w.B, w.H, d_v), dtype=torch.bfloat16, device=dev)
+        for name, fn, nbytes in (
+                ("mla_absorb_q", lambda: m.attn_mla_absorb_q(qh, w_uk, q_lat),
+                 2 * (w.B * w.H * d_h + w.H * w.d_c * d_h + w.B * w.H * w.d_c)),
+                ("mla_up_v", lambda: m.attn_mla_up_v(out, w_uv, o),
+                 2 * (w.B * w.H * w.d_c + w.H * w.d_c * d_v + w.B * w.H * d_v))):
+            us = _time_calls(fn, stream, warmup, iters)
+            flops = 2 * w.B * w.H * d_h * w.d_c
+            res[name] = {"workload": f"B={w.B}, H={w.H}, d_c={w.d_c}, d_head=128, bf16 weights [H, d_c, 128]",
+                         "us": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                         "TFLOPs": round(flops / (us * 1e-6) / 1e12, 2)}
     return res
 
 

@@ -282,6 +282,26 @@ int attn_decode_mla_partial(const void* q_nope_absorbed, const void* q_rope,
                             int partition_size, float* part_out, float* part_lse,
                             hipStream_t stream);
 
+/* ---------------------------------------------------------------- MLA absorption products
+ * The per-head matrix products on either side of the absorbed MLA decode
+ * ("Attention variants: MQA, GQA, and MLA", section "MLA: cache a latent, not
+ * the keys and values": the key up-projection is absorbed into the query,
+ * the value up-projection is applied to the averaged latent). Weights use
+ * the page's layout [H, d_c, d_head]. bf16 in, fp32 accumulation on the
+ * matrix cores, bf16 out (round to nearest even).
+ *
+ * attn_mla_absorb_q:  q_lat[b, h, c] = sum_d q_nope[b, h, d] * w_uk[h, c, d]
+ *   q_nope [B, H, d_h], w_uk [H, d_c, d_h], q_lat [B, H, d_c] (the decode's
+ *   q_nope_absorbed). d_h a multiple of 16, d_c a multiple of 32.
+ * attn_mla_up_v:  out[b, h, d] = sum_c o_lat[b, h, c] * w_uv[h, c, d]
+ *   o_lat [B, H, d_c] (the decode's output), w_uv [H, d_c, d_v], out
+ *   [B, H, d_v]. d_c a multiple of 16, d_v a multiple of 32.
+ * The output must not overlap the inputs. */
+int attn_mla_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, int B, int H, int d_h,
+                      int d_c, hipStream_t stream);
+int attn_mla_up_v(const void* o_lat, const void* w_uv, void* out, int B, int H, int d_c, int d_v,
+                  hipStream_t stream);
+
 #ifdef __cplusplus
 }  /* extern "C" */
 #endif

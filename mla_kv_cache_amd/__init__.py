@@ -29,6 +29,7 @@ __all__ = [
     "attn_decode_gqa_step", "attn_kv_append", "attn_decode_mla_step", "attn_latent_append",
     "attn_decode_gqa_window", "attn_decode_gqa_paged", "attn_kv_append_paged",
     "attn_decode_mla_paged", "attn_latent_append_paged",
+    "attn_mla_absorb_q", "attn_mla_up_v",
 ]
 
 
@@ -438,3 +439,43 @@ def attn_latent_append_paged(latent_new, latent_pages, block_table, seq_lens, d_
                                            _ptr(seq_lens), B, int(d_c), W - int(d_c), num_pages,
                                            page_size, max_pages, _stream(dev)),
            "attn_latent_append_paged")
+
+
+# ----------------------------------------------------------------------------- MLA absorption products
+
+def _bf16_3d(*ts):
+    for t in ts:
+        if t.dtype != torch.bfloat16 or t.dim() != 3:
+            raise ValueError("expected bfloat16 tensors of rank 3")
+
+
+def attn_mla_absorb_q(q_nope, w_uk, out: Optional[torch.Tensor] = None):
+    """q_nope [B,H,d_h] and W_UK [H,d_c,d_h] -> q_lat [B,H,d_c] (bf16, fp32 accumulation)."""
+    _bf16_3d(q_nope, w_uk)
+    B, H, d_h = q_nope.shape
+    if w_uk.shape[0] != H or w_uk.shape[2] != d_h:
+        raise ValueError("W_UK must be [H, d_c, d_h]")
+    d_c = w_uk.shape[1]
+    dev = _dev(q_nope, w_uk)
+    if out is None:
+        out = torch.empty((B, H, d_c), dtype=torch.bfloat16, device=dev)
+    _dev(out)
+    _check(load().attn_mla_absorb_q(_ptr(q_nope), _ptr(w_uk), _ptr(out), B, H, d_h, d_c, _stream(dev)),
+           "attn_mla_absorb_q")
+    return out
+
+
+def attn_mla_up_v(o_lat, w_uv, out: Optional[torch.Tensor] = None):
+    """o_lat [B,H,d_c] and W_UV [H,d_c,d_v] -> out [B,H,d_v] (bf16, fp32 accumulation)."""
+    _bf16_3d(o_lat, w_uv)
+    B, H, d_c = o_lat.shape
+    if w_uv.shape[0] != H or w_uv.shape[1] != d_c:
+        raise ValueError("W_UV must be [H, d_c, d_v]")
+    d_v = w_uv.shape[2]
+    dev = _dev(o_lat, w_uv)
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=torch.bfloat16, device=dev)
+    _dev(out)
+    _check(load().attn_mla_up_v(_ptr(o_lat), _ptr(w_uv), _ptr(out), B, H, d_c, d_v, _stream(dev)),
+           "attn_mla_up_v")
+    return out

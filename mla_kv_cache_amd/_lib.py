@@ -57,6 +57,8 @@ SIGNATURES = {
     "attn_kv_append_paged": (_c_int, [_vp] * 6 + [_c_int] * 7 + [_vp]),
     "attn_decode_mla_paged": (_c_int, [_vp] * 5 + [_c_int] * 7 + [_c_float, _vp, _vp, _c_size, _vp]),
     "attn_latent_append_paged": (_c_int, [_vp] * 4 + [_c_int] * 6 + [_vp]),
+    "attn_mla_absorb_q": (_c_int, [_vp, _vp, _vp] + [_c_int] * 4 + [_vp]),
+    "attn_mla_up_v": (_c_int, [_vp, _vp, _vp] + [_c_int] * 4 + [_vp]),
 }
 
 _lock = threading.Lock()

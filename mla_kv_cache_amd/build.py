@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libattn_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["attn_decode.cpp", "gqa_decode.hip", "lse_merge.hip", "mla_decode.hip"]
+SOURCES = ["attn_decode.cpp", "gqa_decode.hip", "lse_merge.hip", "mla_decode.hip", "mla_absorb.hip"]
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are switched off for all device code.

@@ -636,4 +636,42 @@ int attn_latent_append(const void* latent_new, void* latent_cache, const int32_t
   return ATTN_OK;
 }
 
+// ------------------------------------------------------------------ MLA absorption products
+
+static int check_absorb_args(const void* x, size_t xb, const void* w, size_t wb, const void* y,
+                             size_t yb) {
+  if (!x || !w || !y) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return ATTN_ERR_UNSUPPORTED;
+  if (overlap(y, yb, x, xb) || overlap(y, yb, w, wb)) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+int attn_mla_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, int B, int H, int d_h,
+                      int d_c, hipStream_t stream) {
+  if (B < 1 || H < 1 || d_h < 1 || d_c < 1 || H > kMaxGridYZ) return ATTN_ERR_INVALID_ARG;
+  if (int64_t(B) * H * (d_h > d_c ? d_h : d_c) >= kMaxElems ||
+      int64_t(H) * d_c * d_h >= kMaxElems)
+    return ATTN_ERR_INVALID_ARG;
+  if (!attn::absorb_supported(d_h, d_c)) return ATTN_ERR_UNSUPPORTED;
+  const int st = check_absorb_args(q_nope, size_t(B) * H * d_h * 2, w_uk, size_t(H) * d_c * d_h * 2,
+                                   q_lat, size_t(B) * H * d_c * 2);
+  if (st != ATTN_OK) return st;
+  if (attn::launch_absorb_q(q_nope, w_uk, q_lat, B, H, d_h, d_c, stream) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+int attn_mla_up_v(const void* o_lat, const void* w_uv, void* out, int B, int H, int d_c, int d_v,
+                  hipStream_t stream) {
+  if (B < 1 || H < 1 || d_c < 1 || d_v < 1 || H > kMaxGridYZ) return ATTN_ERR_INVALID_ARG;
+  if (int64_t(B) * H * (d_c > d_v ? d_c : d_v) >= kMaxElems ||
+      int64_t(H) * d_c * d_v >= kMaxElems)
+    return ATTN_ERR_INVALID_ARG;
+  if (!attn::up_supported(d_c, d_v)) return ATTN_ERR_UNSUPPORTED;
+  const int st = check_absorb_args(o_lat, size_t(B) * H * d_c * 2, w_uv, size_t(H) * d_c * d_v * 2,
+                                   out, size_t(B) * H * d_v * 2);
+  if (st != ATTN_OK) return st;
+  if (attn::launch_up_v(o_lat, w_uv, out, B, H, d_c, d_v, stream) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
 }  // extern "C"

@@ -79,4 +79,12 @@ hipError_t launch_append_paged(const void* new_a, const void* new_b, void* pages
                                int heads, int row_bytes, int page_size, int max_pages,
                                int num_pages, hipStream_t stream);
 
+// MLA absorption products (bf16 in, fp32 accumulation, bf16 out).
+bool absorb_supported(int d_h, int d_c);
+bool up_supported(int d_c, int d_v);
+hipError_t launch_absorb_q(const void* q, const void* w_uk, void* q_lat, int B, int H, int d_h,
+                           int d_c, hipStream_t stream);
+hipError_t launch_up_v(const void* o_lat, const void* w_uv, void* out, int B, int H, int d_c,
+                       int d_v, hipStream_t stream);
+
 }  // namespace attn

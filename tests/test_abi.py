@@ -263,3 +263,15 @@ def test_paged_argument_checks(lib):
     la = lib.attn_latent_append_paged
     assert la(KN, P16c, BT, LENS, 4, 512, 60, 64, 64, 16, None) == UNSUPPORTED
 
+
+
+def test_absorb_argument_checks(lib):
+    a, u = lib.attn_mla_absorb_q, lib.attn_mla_up_v
+    assert a(P16, P16b, OUT, 0, 128, 128, 512, None) == INVALID
+    assert a(NULL, P16b, OUT, 64, 128, 128, 512, None) == INVALID
+    assert a(P16, P16b, OUT, 64, 128, 120, 512, None) == UNSUPPORTED      # d_h not a multiple of 16
+    assert a(P16, P16b, OUT, 64, 128, 128, 500, None) == UNSUPPORTED      # d_c not a multiple of 32
+    assert a(P16, P16b, P16b, 64, 128, 128, 512, None) == INVALID         # output over the weights
+    assert a(ctypes.c_void_p((1 << 20) + 2), P16b, OUT, 64, 128, 128, 512, None) == UNSUPPORTED
+    assert u(P16, P16b, OUT, 64, 128, 512, 100, None) == UNSUPPORTED      # d_v not a multiple of 32
+    assert u(P16, P16b, P16, 64, 128, 512, 128, None) == INVALID          # output over o_lat

@@ -60,13 +60,17 @@ int check_gqa_shape(const GqaShape& s) {
   return ATTN_OK;
 }
 
-// Positions per partition: a power of two in [512, 4096] chosen so that the
-// (b, kv head, partition) grid holds about 8192 work-groups (32 per CU on the
-// 256-CU part) when the cache is full. A work-group's 4 waves take 64-position
-// tiles in turn, so 512 positions give each wave two tiles.
+// Positions per partition: a power of two in [512, 4096]. The persistent
+// kernel splits the non-empty partitions evenly over its resident
+// work-groups (512 on the 256-CU part), so it aims for about 2048 partitions
+// when the cache is full: few enough that each work-group's share is long
+// (every partition ends with a combine of its 4 waves), enough that the
+// share of a ragged batch still splits evenly. The per-partition grid
+// kernel aims for about 8192 work-groups (32 per CU).
 int gqa_auto_partition(const GqaShape& s) {
   const int64_t pairs = int64_t(s.B) * s.h_kv;
-  const int64_t want = (int64_t(s.T_max) * pairs + 8191) / 8192;
+  const int64_t target = attn::gqa_persistent(int(s.dt), s.D, s.h_q / s.h_kv) ? 2048 : 8192;
+  const int64_t want = (int64_t(s.T_max) * pairs + target - 1) / target;
   int P = 512;
   while (P < want && P < 4096) P <<= 1;
   return P;

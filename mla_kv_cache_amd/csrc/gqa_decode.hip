@@ -26,6 +26,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "device_util.h"
@@ -527,6 +528,94 @@ constexpr int kBufWord3 = 0x00020000;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Work items of the persistent partial kernel: (sequence b, KV head j,
+// partition p) for every partition that holds at least one attended
+// position, numbered sequence-major (b, then j, then p). Work-group w of G
+// takes the contiguous run [w * N / G, (w + 1) * N / G) of the N items, so
+// every work-group gets the same number of partitions (give or take one)
+// whatever the mix of sequence lengths, and consecutive items mostly share
+// one query and one KV head.
+struct ItemRun {
+  long long left;  // items still to do, the current one included
+  int b, j, p;     // current item
+  int np;          // partitions of sequence b
+};
+
+__device__ __forceinline__ int partitions_of(const GqaArgs& a, int b) {
+  const int n = attended_len(a.seq_lens[b], a.k_new ? 1 : 0, a.T_max);
+  return (int)(((long long)n - window_lo(n, a.window) + a.P - 1) / a.P);
+}
+
+__device__ __forceinline__ long long wave_sum_ll(long long x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__device__ __forceinline__ long long wave_incl_scan_ll(long long x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ long long uniform_ll(long long x) {
+  const uint64_t u = (uint64_t)x;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (long long)(((uint64_t)hi << 32) | lo);
+}
+
+// This work-group's first item and item count. Every wave computes the same
+// (uniform) answer from the sequence lengths, 64 sequences at a time.
+__device__ ItemRun first_item(const GqaArgs& a) {
+  const int lane = threadIdx.x & 63;
+  ItemRun r{0, 0, 0, 0, 0};
+  long long total = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int b = b0 + lane;
+    total += wave_sum_ll(b < a.B ? (long long)partitions_of(a, b) : 0);
+  }
+  total = uniform_ll(total * a.h_kv);
+  const long long lo = total * blockIdx.x / gridDim.x;
+  const long long hi = total * (blockIdx.x + 1) / gridDim.x;
+  if (hi <= lo) return r;
+  long long base = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int b = b0 + lane;
+    const int np = b < a.B ? partitions_of(a, b) : 0;
+    const long long cnt = (long long)np * a.h_kv;
+    const long long incl = base + wave_incl_scan_ll(cnt, lane);
+    const uint64_t hit = __ballot(incl > lo);
+    if (hit) {
+      const int l0 = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+      const long long excl = uniform_ll(__shfl(incl - cnt, l0, 64));
+      r.np = __builtin_amdgcn_readfirstlane(__shfl(np, l0, 64));
+      r.b = b0 + l0;
+      const long long off = lo - excl;
+      r.j = (int)(off / r.np);
+      r.p = (int)(off % r.np);
+      r.left = hi - lo;
+      return r;
+    }
+    base = uniform_ll(__shfl(incl, 63, 64));
+  }
+  return r;
+}
+
+// The item after the current one (sequences without partitions are skipped).
+__device__ __forceinline__ void next_item(ItemRun& r, const GqaArgs& a) {
+  if (++r.p < r.np) return;
+  r.p = 0;
+  if (++r.j < a.h_kv) return;
+  r.j = 0;
+  do {
+    ++r.b;
+  } while (r.b < a.B && (r.np = partitions_of(a, r.b)) == 0);
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs a) {
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
@@ -548,79 +637,14 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
 
   __shared__ __attribute__((aligned(1024))) unsigned char ktile[kWaves][KBYTES];
   __shared__ __attribute__((aligned(16))) float wtab[kWaves][kPoRows][GP];
-
-  const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  const int len0 = a.seq_lens[b];
-  const int n = attended_len(len0, a.k_new ? 1 : 0, T_max);
-  const int start = window_lo(n, a.window) + p * P;
-  if (start >= n) return;
-  const int end = min(start, n - P) + P;
-  if (a.k_new) {  // decode step: the work-group that reads the new row writes it first
-    const int pos = max(len0, 0);
-    if (pos < T_max && pos >= start && pos < end) {
-      const size_t row = (((size_t)b * h_kv + j) * (size_t)T_max + pos) * D;
-      const size_t src = ((size_t)b * h_kv + j) * D;
-      write_row_then_sync<D * 2>(const_cast<uint16_t*>(kc) + row, static_cast<const uint16_t*>(a.k_new) + src);
-      write_row_then_sync<D * 2>(const_cast<uint16_t*>(vc) + row, static_cast<const uint16_t*>(a.v_new) + src);
-    }
-  }
+  __shared__ float sm_m[kWaves][G];
+  __shared__ float sm_l[kWaves][G];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   const int rr = lane / LPR, c = lane % LPR;
   const int H = h_kv * G;
-
-  // Query of the G heads as packed bf16 pairs. For G = 1 it is read with
-  // uniform addresses (scalar loads: it fits the scalar registers). For
-  // G >= 2 it would not, so it is spread over vector registers instead:
-  // word w sits in register w / 16 of lane w % 16 of every 16-lane row, and
-  // each dot product fetches it with a row broadcast (dot_chunk2/4/8).
-  constexpr bool kBcastQ = G >= 2;
-  constexpr int QR = kBcastQ ? G * D / 32 : 1;
-  const uint32_t* qw = reinterpret_cast<const uint32_t*>(q + ((size_t)b * H + (size_t)j * G) * D);
-  uint32_t qd[QR];
-#pragma unroll
-  for (int r = 0; r < QR; ++r) qd[r] = kBcastQ ? qw[16 * r + (threadIdx.x & 15)] : 0u;
-
-  float m[G], lpart[G], acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegInf;
-    lpart[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  }
-
-  // Buffer resources over this (sequence, KV head) slab, limited to the
-  // sequence's valid rows: a read at or past row n returns zeros, so the
-  // tail of the last tile needs no clamping and padding rows are never
-  // fetched. Byte offsets fit 32 bits (the host limits T_max * D * 2).
-  // A paged cache gets one pair of resources per tile instead (tile_rsrc).
   const bool paged = a.block_table != nullptr;
-  const size_t head_off = paged ? 0 : ((size_t)b * h_kv + j) * (size_t)T_max * D;
-  const int valid_bytes = n * (D * 2);
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + head_off), 0, valid_bytes, kBufWord3);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + head_off), 0, valid_bytes, kBufWord3);
-  // Paged: the 64 rows of a tile lie in one page (page_size is a multiple of
-  // 64 and tiles start at multiples of 64); its resources cover the tile's
-  // rows below n, and a table entry outside [0, num_pages) reads as zeros.
-  auto tile_rsrc = [&](int t0, __amdgpu_buffer_rsrc_t& kr, __amdgpu_buffer_rsrc_t& vr_, uint32_t& toff) {
-    if (!paged) {
-      kr = krs;
-      vr_ = vrs;
-      toff = (uint32_t)t0 * (D * 2);
-      return;
-    }
-    const int phys = a.block_table[(size_t)b * a.max_pages + (t0 >> a.page_shift)];
-    const bool ok = phys >= 0 && phys < a.num_pages;
-    const int rows = ok ? min(kPoRows, n - t0) : 0;
-    const size_t off = (((size_t)(ok ? phys : 0) * h_kv + j) * a.page_size + (t0 & (a.page_size - 1))) * D;
-    kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + off), 0, rows * (D * 2), kBufWord3);
-    vr_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + off), 0, rows * (D * 2), kBufWord3);
-    toff = 0;
-  };
   const uint32_t kt_lds = __builtin_amdgcn_readfirstlane(lds_addr(&ktile[wave][0]));
   const unsigned char* kt = &ktile[wave][0];
   float* wt = &wtab[wave][0][0];
@@ -654,181 +678,281 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
     return make_uint4(w.x, w.y, w.z, w.w);
   };
 
-  for (int t0 = start + wave * kPoRows; t0 < end; t0 += kWaves * kPoRows) {
-    __amdgpu_buffer_rsrc_t krt, vrt;
-    uint32_t toff;
-    tile_rsrc(t0, krt, vrt, toff);
-    copy_k(krt, toff);
-    uint4 vr[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) vr[i] = load_v(vrt, toff, i);
-    // The K copies were issued first: once at most NV memory operations of
-    // this wave are outstanding, they have all landed.
-    if constexpr (NV == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if constexpr (NV == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Query of the G heads as packed bf16 pairs. For G = 1 it is read with
+  // uniform addresses (scalar loads: it fits the scalar registers). For
+  // G >= 2 it would not, so it is spread over vector registers instead:
+  // word w sits in register w / 16 of lane w % 16 of every 16-lane row, and
+  // each dot product fetches it with a row broadcast (dot_chunk2/4/8).
+  constexpr bool kBcastQ = G >= 2;
+  constexpr int QR = kBcastQ ? G * D / 32 : 1;
+  uint32_t qd[QR];
+  int qb = -1, qj = -1;  // (sequence, KV head) whose query qd holds
 
-    // ---- scores: lane owns position t0 + lane; its K row comes out of LDS
-    // in one batch, then G dot products run on it.
-    const unsigned char* krow = kt + lane * (D * 2);
-    float s[G];
+  for (ItemRun run = first_item(a); run.left > 0 && run.b < a.B;) {
+    const int b = run.b, j = run.j, p = run.p;
+    const int len0 = a.seq_lens[b];
+    const int n = attended_len(len0, a.k_new ? 1 : 0, T_max);
+    const int start = window_lo(n, a.window) + p * P;
+    const int end = min(start, n - P) + P;
+    if (a.k_new) {  // decode step: the work-group that reads the new row writes it first
+      const int pos = max(len0, 0);
+      if (pos < T_max && pos >= start && pos < end) {
+        const size_t row = (((size_t)b * h_kv + j) * (size_t)T_max + pos) * D;
+        const size_t src = ((size_t)b * h_kv + j) * D;
+        write_row_then_sync<D * 2>(const_cast<uint16_t*>(kc) + row, static_cast<const uint16_t*>(a.k_new) + src);
+        write_row_then_sync<D * 2>(const_cast<uint16_t*>(vc) + row, static_cast<const uint16_t*>(a.v_new) + src);
+      }
+    }
+
+    const uint32_t* qw = reinterpret_cast<const uint32_t*>(q + ((size_t)b * H + (size_t)j * G) * D);
+    if (kBcastQ && (b != qb || j != qj)) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[h] = 0.f;
-    // The row is read from LDS in KS slices of CH / KS chunks, each used at
-    // once, so only one slice is held in registers beside the V tile.
-    constexpr int KS = G >= 4 ? 2 : 1;
-    constexpr int CS = CH / KS;
-    static_for<KS>([&](auto ks_) {
-      constexpr int ks = decltype(ks_)::value;
-      uint4 kk[CS];
-#pragma unroll
-      for (int u = 0; u < CS; ++u)
-        kk[u] = *reinterpret_cast<const uint4*>(krow + 16 * ((ks * CS + u) ^ (lane % CH)));
-      static_for<CS>([&](auto u_) {
-        constexpr int u = decltype(u_)::value;
-        constexpr int jc = ks * CS + u;
-        if constexpr (kBcastQ) {
-          // Query word h*D/2 + 4*jc + e is register (h*D/2 + 4*jc) / 16,
-          // row lane 4*(jc % 4) + e.
-          constexpr int l0 = 4 * (jc % 4);
-          uint32_t qr[G];
-#pragma unroll
-          for (int h = 0; h < G; ++h) qr[h] = qd[(h * (D / 2) + 4 * jc) / 16];
-          if constexpr (G == 2) dot_chunk2<l0>(s, qr, kk[u]);
-          else if constexpr (G == 4) dot_chunk4<l0>(s, qr, kk[u]);
-          else dot_chunk8<l0>(s, qr, kk[u]);
-        } else {
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const uint32_t* qh = qw + h * (D / 2) + 4 * jc;
-            float a = s[h];
-            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[0]), __builtin_bit_cast(bf16x2, kk[u].x), a, false);
-            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[1]), __builtin_bit_cast(bf16x2, kk[u].y), a, false);
-            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[2]), __builtin_bit_cast(bf16x2, kk[u].z), a, false);
-            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[3]), __builtin_bit_cast(bf16x2, kk[u].w), a, false);
-            s[h] = a;
-          }
-        }
-      });
-      // Keep the next slice's reads below this slice's arithmetic.
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    // The K area is rewritten by the next tile's copy: all its reads are done.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const bool valid = t0 + lane < end;
-    bool need = false;
-    float mx[G];
+      for (int r = 0; r < QR; ++r) qd[r] = qw[16 * r + (threadIdx.x & 15)];
+      qb = b;
+      qj = j;
+    }
+
+    float m[G], lpart[G], acc[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      s[h] = valid ? s[h] * qk_scale_log2 : kNegInf;
-      mx[h] = s[h];
-    }
-    if constexpr (G == 4) {
-      wave_max4(mx);
-    } else if constexpr (G == 8) {
-      wave_max8(mx);
-    } else {
+      m[h] = kNegInf;
+      lpart[h] = 0.f;
 #pragma unroll
-      for (int h = 0; h < G; ++h) mx[h] = wave_max(mx[h]);
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     }
+
+    // Buffer resources over this (sequence, KV head) slab, limited to the
+    // sequence's valid rows: a read at or past row n returns zeros, so the
+    // tail of the last tile needs no clamping and padding rows are never
+    // fetched. Byte offsets fit 32 bits (the host limits T_max * D * 2).
+    // A paged cache gets one pair of resources per tile instead (tile_rsrc).
+    const size_t head_off = paged ? 0 : ((size_t)b * h_kv + j) * (size_t)T_max * D;
+    const int valid_bytes = n * (D * 2);
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + head_off), 0, valid_bytes, kBufWord3);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + head_off), 0, valid_bytes, kBufWord3);
+    // Paged: the 64 rows of a tile lie in one page (page_size is a multiple of
+    // 64 and tiles start at multiples of 64); its resources cover the tile's
+    // rows below n, and a table entry outside [0, num_pages) reads as zeros.
+    auto tile_rsrc = [&](int t0, __amdgpu_buffer_rsrc_t& kr, __amdgpu_buffer_rsrc_t& vr_, uint32_t& toff) {
+      if (!paged) {
+        kr = krs;
+        vr_ = vrs;
+        toff = (uint32_t)t0 * (D * 2);
+        return;
+      }
+      const int phys = a.block_table[(size_t)b * a.max_pages + (t0 >> a.page_shift)];
+      const bool ok = phys >= 0 && phys < a.num_pages;
+      const int rows = ok ? min(kPoRows, n - t0) : 0;
+      const size_t off = (((size_t)(ok ? phys : 0) * h_kv + j) * a.page_size + (t0 & (a.page_size - 1))) * D;
+      kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + off), 0, rows * (D * 2), kBufWord3);
+      vr_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + off), 0, rows * (D * 2), kBufWord3);
+      toff = 0;
+    };
+
+    for (int t0 = start + wave * kPoRows; t0 < end; t0 += kWaves * kPoRows) {
+      __amdgpu_buffer_rsrc_t krt, vrt;
+      uint32_t toff;
+      tile_rsrc(t0, krt, vrt, toff);
+      copy_k(krt, toff);
+      uint4 vr[NV];
 #pragma unroll
-    for (int h = 0; h < G; ++h) need |= mx[h] > m[h] + kTau;
-    if (need) {  // wave-uniform: the maxima are wave-wide
+      for (int i = 0; i < NV; ++i) vr[i] = load_v(vrt, toff, i);
+      // The K copies were issued first: once at most NV memory operations of
+      // this wave are outstanding, they have all landed.
+      if constexpr (NV == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      else if constexpr (NV == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+      // ---- scores: lane owns position t0 + lane; its K row comes out of LDS
+      // in one batch, then G dot products run on it.
+      const unsigned char* krow = kt + lane * (D * 2);
+      float s[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[h] = 0.f;
+      // The row is read from LDS in KS slices of CH / KS chunks, each used at
+      // once, so only one slice is held in registers beside the V tile.
+      constexpr int KS = G >= 4 ? 2 : 1;
+      constexpr int CS = CH / KS;
+      static_for<KS>([&](auto ks_) {
+        constexpr int ks = decltype(ks_)::value;
+        uint4 kk[CS];
+#pragma unroll
+        for (int u = 0; u < CS; ++u)
+          kk[u] = *reinterpret_cast<const uint4*>(krow + 16 * ((ks * CS + u) ^ (lane % CH)));
+        static_for<CS>([&](auto u_) {
+          constexpr int u = decltype(u_)::value;
+          constexpr int jc = ks * CS + u;
+          if constexpr (kBcastQ) {
+            // Query word h*D/2 + 4*jc + e is register (h*D/2 + 4*jc) / 16,
+            // row lane 4*(jc % 4) + e.
+            constexpr int l0 = 4 * (jc % 4);
+            uint32_t qr[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) qr[h] = qd[(h * (D / 2) + 4 * jc) / 16];
+            if constexpr (G == 2) dot_chunk2<l0>(s, qr, kk[u]);
+            else if constexpr (G == 4) dot_chunk4<l0>(s, qr, kk[u]);
+            else dot_chunk8<l0>(s, qr, kk[u]);
+          } else {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              const uint32_t* qh = qw + h * (D / 2) + 4 * jc;
+              float a = s[h];
+              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[0]), __builtin_bit_cast(bf16x2, kk[u].x), a, false);
+              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[1]), __builtin_bit_cast(bf16x2, kk[u].y), a, false);
+              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[2]), __builtin_bit_cast(bf16x2, kk[u].z), a, false);
+              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[3]), __builtin_bit_cast(bf16x2, kk[u].w), a, false);
+              s[h] = a;
+            }
+          }
+        });
+        // Keep the next slice's reads below this slice's arithmetic.
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // The K area is rewritten by the next tile's copy: all its reads are done.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const bool valid = t0 + lane < end;
+      bool need = false;
+      float mx[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const bool nh = mx[h] > m[h] + kTau;
-        const float f = nh ? fast_exp2(m[h] - mx[h]) : 1.f;
-        m[h] = nh ? mx[h] : m[h];
-        lpart[h] *= f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= f;
+        s[h] = valid ? s[h] * qk_scale_log2 : kNegInf;
+        mx[h] = s[h];
       }
-    }
-    float w[GP];
+      if constexpr (G == 4) {
+        wave_max4(mx);
+      } else if constexpr (G == 8) {
+        wave_max8(mx);
+      } else {
 #pragma unroll
-    for (int h = 0; h < GP; ++h) {
-      w[h] = (h < G && valid) ? fast_exp2(s[h < G ? h : 0] - m[h < G ? h : 0]) : 0.f;
-      if (h < G) lpart[h] += w[h];
-    }
-#pragma unroll
-    for (int h = 0; h < GP; h += 4)
-      *reinterpret_cast<float4*>(wt + lane * GP + h) = make_float4(w[h], w[h + 1], w[h + 2], w[h + 3]);
-
-    // ---- output: lane (rr, c) accumulates rows i*RPI + rr, dims 8c .. 8c+7
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const float* wr = wt + (i * RPI + rr) * GP;
-      float wv[GP];
-#pragma unroll
-      for (int h = 0; h < GP; h += 4) {
-        const float4 t = *reinterpret_cast<const float4*>(wr + h);
-        wv[h] = t.x;
-        wv[h + 1] = t.y;
-        wv[h + 2] = t.z;
-        wv[h + 3] = t.w;
+        for (int h = 0; h < G; ++h) mx[h] = wave_max(mx[h]);
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t wd = word(vr[i], e >> 1);
-        const float x = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+      for (int h = 0; h < G; ++h) need |= mx[h] > m[h] + kTau;
+      if (need) {  // wave-uniform: the maxima are wave-wide
 #pragma unroll
-        for (int h = 0; h < G; ++h) acc[h][e] = fmaf(wv[h], x, acc[h][e]);
+        for (int h = 0; h < G; ++h) {
+          const bool nh = mx[h] > m[h] + kTau;
+          const float f = nh ? fast_exp2(m[h] - mx[h]) : 1.f;
+          m[h] = nh ? mx[h] : m[h];
+          lpart[h] *= f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] *= f;
+        }
+      }
+      float w[GP];
+#pragma unroll
+      for (int h = 0; h < GP; ++h) {
+        w[h] = (h < G && valid) ? fast_exp2(s[h < G ? h : 0] - m[h < G ? h : 0]) : 0.f;
+        if (h < G) lpart[h] += w[h];
+      }
+#pragma unroll
+      for (int h = 0; h < GP; h += 4)
+        *reinterpret_cast<float4*>(wt + lane * GP + h) = make_float4(w[h], w[h + 1], w[h + 2], w[h + 3]);
+
+      // ---- output: lane (rr, c) accumulates rows i*RPI + rr, dims 8c .. 8c+7
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const float* wr = wt + (i * RPI + rr) * GP;
+        float wv[GP];
+#pragma unroll
+        for (int h = 0; h < GP; h += 4) {
+          const float4 t = *reinterpret_cast<const float4*>(wr + h);
+          wv[h] = t.x;
+          wv[h + 1] = t.y;
+          wv[h + 2] = t.z;
+          wv[h + 3] = t.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t wd = word(vr[i], e >> 1);
+          const float x = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+#pragma unroll
+          for (int h = 0; h < G; ++h) acc[h][e] = fmaf(wv[h], x, acc[h][e]);
+        }
       }
     }
-  }
 
-  // All lanes of a wave share m: the row groups add up, the per-position sums add up.
-  float L[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    L[h] = wave_sum(lpart[h]);
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, 64);
-  }
-
-  // Combine the waves through LDS and write this partition's partial. The
-  // per-wave sums reuse the K tile area once every wave has left its loop.
-  static_assert(sizeof(float) * kWaves * G * D <= sizeof(ktile), "combine area too small");
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
-  __syncthreads();
-  float (*sm_acc)[G][D] = reinterpret_cast<float (*)[G][D]>(&ktile[0][0]);
-  if (lane < LPR) {
+    // All lanes of a wave share m: the row groups add up, the per-position sums add up.
+    float L[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+      L[h] = wave_sum(lpart[h]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm_acc[wave][h][c * 8 + e] = acc[h][e];
-      if (c == 0) {
-        sm_m[wave][h] = m[h];
-        sm_l[wave][h] = L[h];
+      for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, 64);
+    }
+
+    // Combine the waves through LDS and write this partition's partial. The
+    // per-wave sums reuse the K tile area once every wave has left its loop.
+    static_assert(sizeof(float) * kWaves * G * D <= sizeof(ktile), "combine area too small");
+    __syncthreads();
+    float (*sm_acc)[G][D] = reinterpret_cast<float (*)[G][D]>(&ktile[0][0]);
+    if (lane < LPR) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm_acc[wave][h][c * 8 + e] = acc[h][e];
+        if (c == 0) {
+          sm_m[wave][h] = m[h];
+          sm_l[wave][h] = L[h];
+        }
       }
     }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int h = idx / D, d = idx % D;
-    float M = sm_m[0][h];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+      const int h = idx / D, d = idx % D;
+      float M = sm_m[0][h];
 #pragma unroll
-    for (int w2 = 1; w2 < kWaves; ++w2) M = fmaxf(M, sm_m[w2][h]);
-    float Ls = 0.f, A = 0.f;
+      for (int w2 = 1; w2 < kWaves; ++w2) M = fmaxf(M, sm_m[w2][h]);
+      float Ls = 0.f, A = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < kWaves; ++w2) {
-      const float mw = sm_m[w2][h];
-      const float f = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
-      Ls += sm_l[w2][h] * f;
-      A += sm_acc[w2][h][d] * f;
+      for (int w2 = 0; w2 < kWaves; ++w2) {
+        const float mw = sm_m[w2][h];
+        const float f = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
+        Ls += sm_l[w2][h] * f;
+        A += sm_acc[w2][h][d] * f;
+      }
+      const size_t row = ((size_t)b * H + (size_t)j * G + h) * NP + p;
+      part_out[row * D + d] = A / Ls;
+      if (d == 0) part_lse[row] = M + fast_log2(Ls);
     }
-    const size_t row = ((size_t)b * H + (size_t)j * G + h) * NP + p;
-    part_out[row * D + d] = A / Ls;
-    if (d == 0) part_lse[row] = M + fast_log2(Ls);
+    __syncthreads();  // the combine area is the next item's K tile area
+    if (--run.left > 0) next_item(run, a);
   }
 }
 
+// Compute units of the current device (looked up once per device).
+int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cus[dev].load(std::memory_order_relaxed) > 0) return cus[dev].load(std::memory_order_relaxed);
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// The persistent kernel is launched with as many work-groups as the device
+// holds at once (never more than there are partitions); each takes an equal
+// share of the non-empty partitions.
 template <int D, int G>
 hipError_t launch_po(const GqaArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((gqa_partial_po_kernel<D, G>), dim3(a.NP, a.h_kv, a.B), dim3(kThreads), 0, stream, a);
+  static const int per_cu = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&gqa_partial_po_kernel<D, G>),
+                                                     kThreads, 0) != hipSuccess || nb < 1)
+      nb = 1;
+    return nb;
+  }();
+  const int cus = device_cus();
+  if (cus <= 0) return hipErrorInvalidDevice;
+  const long long items = (long long)a.B * a.h_kv * a.NP;
+  const int grid = (int)std::min<long long>(items, (long long)cus * per_cu);
+  hipLaunchKernelGGL((gqa_partial_po_kernel<D, G>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -893,6 +1017,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const unsigned char* __r
 }
 
 }  // namespace
+
+bool gqa_persistent(int dt, int D, int group) {
+  return dt == 1 && (D == 64 || D == 128) && group >= kPoMinGroup && group <= 8 && (group & (group - 1)) == 0;
+}
 
 bool gqa_supported(int dt, int D, int group) {
   const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8 || group == 16;

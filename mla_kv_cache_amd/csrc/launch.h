@@ -9,6 +9,9 @@ namespace attn {
 
 // dt: 0 = fp32 storage, 1 = bf16 storage (values of attn_dtype).
 bool gqa_supported(int dt, int D, int group);
+// True when a contiguous-cache decode of this shape runs on the persistent
+// position-per-lane kernel (one work-group per resident slot).
+bool gqa_persistent(int dt, int D, int group);
 
 // Arguments of the GQA partial kernels (passed by value as kernel arguments).
 struct GqaArgs {

@@ -187,7 +187,7 @@ def test_full_size_plans_fill_the_chip(lib):
         P, NP = ctypes.c_int(), ctypes.c_int()
         assert lib.attn_decode_gqa_plan(B, hq, hkv, 128, T, BF16, ctypes.byref(P), ctypes.byref(NP),
                                         None) == OK
-        assert B * hkv * NP.value >= 1024        # at least 4 work-groups per CU on 256 CUs
+        assert B * hkv * NP.value >= 1024        # at least 2 partitions per resident work-group (512)
 
 
 def test_step_and_append_argument_checks(lib):

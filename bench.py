@@ -392,7 +392,7 @@ def main():
 
             def merge(po=po, pl=pl, gl=gl, P=P, out=out, w=w):
                 m.attn_decode_merge(po, pl, gl, w.T_max, P, out=out)
-            kname = f"mla_partial_kernel<{4 if w.H >= 128 else w.H // 32}>"
+            kname = f"mla_partial_kernel<{4 if w.H >= 128 else w.H // 32}, false>"
             src = os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "mla_decode.hip")
         items.append(dict(name=name, kind=kind, w=w, partial=partial, merge=merge, kv=kv,
                           other=other, flops=flops, P=P, NP=NP, kname=kname, src=src,

@@ -176,8 +176,8 @@ int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_
  * A sequence holds at most T_max = max_pages * page_size positions (seq_lens
  * clamped to it); entries past a sequence's last used page are never read,
  * and pages may be shared between sequences (read-only here). page_size: a
- * power of two >= 16; the fast bf16 kernel (g <= 8) needs a multiple of 64,
- * smaller pages go through a slower per-row gather. A used table entry outside
+ * power of two >= 16; the fast bf16 kernel (g <= 8) needs a multiple of 32,
+ * 16-row pages go through a slower per-row gather. A used table entry outside
  * [0, num_pages) never faults: its rows read as zeros (or as a clamped page on
  * the per-row path) and the result for that sequence is unspecified.
  * Workspace: attn_decode_gqa_workspace_bytes(B, h_q, h_kv, D, T_max, dt). */

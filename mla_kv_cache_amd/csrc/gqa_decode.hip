@@ -1,17 +1,21 @@
 // Split-KV decode attention for the MHA / GQA / MQA family on gfx950.
 //
-// One work-group (4 wave64s) owns one (sequence b, KV head j, partition p)
-// triple and streams the K and V rows of positions [p*P, min(p*P+P, n)) from
-// HBM exactly once. Every row it loads serves all G = h_q / h_kv query heads
-// of the group (query head i reads KV head i / G, "Attention variants: MQA,
+// A work-group (4 wave64s) streams the K and V rows of one (sequence b, KV
+// head j, partition p) triple, positions [p*P, min(p*P+P, n)), from HBM
+// exactly once. Every row it loads serves all G = h_q / h_kv query heads of
+// the group (query head i reads KV head i / G, "Attention variants: MQA,
 // GQA, and MLA", section "GQA: interpolating with groups"), so the bytes
-// streamed per step are the cache's own size, not G times it.
+// streamed per step are the cache's own size, not G times it. The bf16
+// kernel (gqa_partial_po_kernel, the second half of this file) is persistent
+// and takes such triples in turn; the general kernel (fp32 caches, groups of
+// 16, pages shorter than its tile) gets one work-group per triple.
 //
-// Data layout in registers: one K (or V) row is D * sizeof(elem) bytes =
-// LPR lanes x 16 bytes, so each 16-byte vector load instruction of a wave
-// covers RPI = 64 / LPR consecutive rows, i.e. one contiguous 1 KiB span.
-// Lane (rr, c) holds elements [c*EPL, c*EPL + EPL) of row rr of each span.
-// Scores reduce over the LPR lanes of a row with DPP moves (no LDS traffic).
+// Data layout in registers of the general kernel: one K (or V) row is
+// D * sizeof(elem) bytes = LPR lanes x 16 bytes, so each 16-byte vector load
+// instruction of a wave covers RPI = 64 / LPR consecutive rows, i.e. one
+// contiguous 1 KiB span. Lane (rr, c) holds elements [c*EPL, c*EPL + EPL) of
+// row rr of each span. Scores reduce over the LPR lanes of a row with DPP
+// moves (no LDS traffic).
 //
 // Softmax is computed online in the exp2 domain (scores pre-multiplied by
 // scale * log2(e)). The running maximum is only moved when a new block's
@@ -256,27 +260,32 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const GqaArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel, one cached position per lane for the scores.
+// bf16 kernel, one cached position per pair of lanes for the scores.
 //
-// Each wave owns tiles of 64 positions (tiles are dealt to the 4 waves in
-// turn). For a tile:
+// The kernel is persistent: as many work-groups as the device holds at once
+// take equal runs of the non-empty (sequence, KV head, partition) items
+// (ItemRun below), so a ragged batch leaves no CU idle. Within an item the 4
+// waves take 32-position tiles in turn. For a tile:
 //  * K rows go straight from HBM into the wave's own LDS area (direct copy,
 //    16 bytes per lane per instruction). Within each row the 16-byte chunks
 //    are stored XOR-permuted by the row index, so that 16 lanes reading the
 //    same logical chunk of 16 different rows hit 16 different bank groups.
-//  * Lane t scores position t0 + t against all G query heads: the query is
-//    the same for every lane, so the compiler keeps it in scalar registers
-//    and each v_dot2 takes it as its scalar operand; no cross-lane reduction.
+//  * Lane l scores position t0 + l % 32 over the dimensions of half l / 32 of
+//    the head, against all G query heads, and the two halves are added with
+//    one lane swap (half_sum). The query words are spread over vector
+//    registers and each v_dot2 fetches its word with a DPP row broadcast.
 //  * The tile maximum per head is one wave-wide reduction; the running
-//    maximum is wave-uniform. Each weight exp2(s - m) is computed once, by
-//    the lane that owns the position, and written to a small LDS table.
+//    maximum is wave-uniform. Each weight exp2(s - m) is written once, by the
+//    lane of half 0 that owns the position, to a small LDS table.
 //  * V rows are loaded into registers in the row layout (LPR lanes x 16 bytes
 //    per row, 1 KiB contiguous per wave-wide load), and each lane reads the G
 //    weights of its row from the table (a broadcast read) for the product.
 // Compared with reducing every score across a row's lanes, the arithmetic per
 // cached element drops from G*(2 + 4/8) lane-ops + G exps per row group to
-// about G/2 dot2 + G/64 exps, which is what matters when G = 4..8.
-constexpr int kPoRows = 64;
+// about G/2 dot2 + G/32 exps, which is what matters when G = 4..8.
+// At the end of an item the 4 waves combine their partials through LDS, with
+// one barrier; the combine area is double-buffered by item parity.
+constexpr int kPoRows = 32;
 
 template <int N, class F, int I = 0>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -522,6 +531,99 @@ __device__ __forceinline__ void wave_max8(float (&x)[8]) {
       : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7]));
 }
 
+template <int L0>
+__device__ __forceinline__ void dot_chunk1(float (&acc)[1], const uint32_t (&qr)[1], const uint4& k) {
+  asm("s_nop 1\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %1, %2 row_newbcast:%6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %1, %3 row_newbcast:%7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %1, %4 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_bf16_dpp %0, %1, %5 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 2"
+      : "+v"(acc[0])
+      : "v"(qr[0]), "v"(k.x), "v"(k.y), "v"(k.z), "v"(k.w), "i"(L0 + 0), "i"(L0 + 1), "i"(L0 + 2), "i"(L0 + 3));
+}
+
+__device__ __forceinline__ void half_sum1(float (&x)[1]) {
+  float t[1];
+  asm(
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %1\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32 %0, %0, %1\n\t"
+      "s_nop 1"
+      : "+v"(x[0]), "=&v"(t[0]));
+}
+
+__device__ __forceinline__ void half_sum2(float (&x)[2]) {
+  float t[2];
+  asm(
+      "v_mov_b32 %2, %0\n\t"
+      "v_mov_b32 %3, %1\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %2\n\t"
+      "v_permlane32_swap_b32 %1, %3\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32 %0, %0, %2\n\t"
+      "v_add_f32 %1, %1, %3\n\t"
+      "s_nop 1"
+      : "+v"(x[0]), "+v"(x[1]), "=&v"(t[0]), "=&v"(t[1]));
+}
+
+__device__ __forceinline__ void half_sum4(float (&x)[4]) {
+  float t[4];
+  asm(
+      "v_mov_b32 %4, %0\n\t"
+      "v_mov_b32 %5, %1\n\t"
+      "v_mov_b32 %6, %2\n\t"
+      "v_mov_b32 %7, %3\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %4\n\t"
+      "v_permlane32_swap_b32 %1, %5\n\t"
+      "v_permlane32_swap_b32 %2, %6\n\t"
+      "v_permlane32_swap_b32 %3, %7\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32 %0, %0, %4\n\t"
+      "v_add_f32 %1, %1, %5\n\t"
+      "v_add_f32 %2, %2, %6\n\t"
+      "v_add_f32 %3, %3, %7\n\t"
+      "s_nop 1"
+      : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]));
+}
+
+__device__ __forceinline__ void half_sum8(float (&x)[8]) {
+  float t[8];
+  asm(
+      "v_mov_b32 %8, %0\n\t"
+      "v_mov_b32 %9, %1\n\t"
+      "v_mov_b32 %10, %2\n\t"
+      "v_mov_b32 %11, %3\n\t"
+      "v_mov_b32 %12, %4\n\t"
+      "v_mov_b32 %13, %5\n\t"
+      "v_mov_b32 %14, %6\n\t"
+      "v_mov_b32 %15, %7\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %8\n\t"
+      "v_permlane32_swap_b32 %1, %9\n\t"
+      "v_permlane32_swap_b32 %2, %10\n\t"
+      "v_permlane32_swap_b32 %3, %11\n\t"
+      "v_permlane32_swap_b32 %4, %12\n\t"
+      "v_permlane32_swap_b32 %5, %13\n\t"
+      "v_permlane32_swap_b32 %6, %14\n\t"
+      "v_permlane32_swap_b32 %7, %15\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32 %0, %0, %8\n\t"
+      "v_add_f32 %1, %1, %9\n\t"
+      "v_add_f32 %2, %2, %10\n\t"
+      "v_add_f32 %3, %3, %11\n\t"
+      "v_add_f32 %4, %4, %12\n\t"
+      "v_add_f32 %5, %5, %13\n\t"
+      "v_add_f32 %6, %6, %14\n\t"
+      "v_add_f32 %7, %7, %15\n\t"
+      "s_nop 1"
+      : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7]));
+}
+
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
 // no swizzle, no stride): loads at or past num_records bytes return zeros.
 constexpr int kBufWord3 = 0x00020000;
@@ -626,33 +728,40 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
   float* __restrict__ part_lse = a.part_lse;
   const int h_kv = a.h_kv, T_max = a.T_max, P = a.P, NP = a.NP;
   const float qk_scale_log2 = a.qk_scale_log2;
+  constexpr int TR = kPoRows;
   constexpr int CH = D / 8;              // 16-byte chunks per row
+  constexpr int HC = CH / 2;             // chunks per half row
   constexpr int LPR = CH;                // lanes per row in the V layout
   constexpr int RPI = 64 / LPR;          // rows per wave-wide V load
-  constexpr int NV = kPoRows / RPI;      // V loads per tile
-  constexpr int KBYTES = kPoRows * D * 2;
+  constexpr int NV = TR / RPI;           // V loads per tile
+  constexpr int KBYTES = TR * D * 2;
   constexpr int NK = KBYTES / 1024;      // K copies per tile (one KiB each)
   constexpr int GP = (G + 3) / 4 * 4;   // weight-table row, padded to whole float4s
-  static_assert(NV <= 32 && NK <= 32, "tile too large");
+  constexpr int WPH = D / 4;             // query words per head and half
+  constexpr int QR = G * WPH / 16;       // query registers
+  static_assert(NK + NV <= 63, "vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) unsigned char ktile[kWaves][KBYTES];
-  __shared__ __attribute__((aligned(16))) float wtab[kWaves][kPoRows][GP];
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
+  __shared__ __attribute__((aligned(16))) float wtab[kWaves][TR][GP];
+  // Per-wave partials of an item, double-buffered by item parity: one
+  // barrier per item then keeps a wave that runs ahead from overwriting a
+  // buffer that is still being combined.
+  __shared__ __attribute__((aligned(16))) float comb[2][kWaves][G][D];
+  __shared__ float sm_m[2][kWaves][G];
+  __shared__ float sm_l[2][kWaves][G];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   const int rr = lane / LPR, c = lane % LPR;
+  const int hf = lane >> 5, pr = lane & 31;
   const int H = h_kv * G;
   const bool paged = a.block_table != nullptr;
   const uint32_t kt_lds = __builtin_amdgcn_readfirstlane(lds_addr(&ktile[wave][0]));
-  const unsigned char* kt = &ktile[wave][0];
   float* wt = &wtab[wave][0][0];
 
-  // K tile -> LDS. Copy i moves rows RPC*i .. RPC*i + RPC - 1 of the tile (one
-  // KiB); its lane l fills LDS chunk 64*i + l, i.e. row RPC*i + l / CH, stored
-  // chunk l % CH, which carries logical chunk (l % CH) ^ (row % CH). The source
-  // offset inside the copy's KiB depends on i only through i % KPER.
+  // K tile -> LDS buffer. Copy i moves rows RPC*i .. RPC*i + RPC - 1 of the
+  // tile (one KiB); its lane l fills LDS chunk 64*i + l, i.e. row RPC*i + l / CH,
+  // stored chunk l % CH, which carries logical chunk (l % CH) ^ (row % CH).
   constexpr int RPC = 1024 / (D * 2);           // rows per copy
   constexpr int KPER = (RPC % CH == 0) ? 1 : CH / RPC;
   uint32_t kvoff[KPER];
@@ -663,11 +772,12 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
     kvoff[mm] = (uint32_t)(rl * D + lc * 8) * 2u;
   }
   auto copy_k = [&](const __amdgpu_buffer_rsrc_t& kr, uint32_t tile_off) {
+    const uint32_t dst = kt_lds;
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       const uint32_t soff = tile_off + 1024u * i;
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                   ::"s"(kt_lds + 1024u * i), "v"(kvoff[i % KPER]), "s"(kr), "s"(soff)
+                   ::"s"(dst + 1024u * i), "v"(kvoff[i % KPER]), "s"(kr), "s"(soff)
                    : "memory");
     }
   };
@@ -678,15 +788,12 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
     return make_uint4(w.x, w.y, w.z, w.w);
   };
 
-  // Query of the G heads as packed bf16 pairs. For G = 1 it is read with
-  // uniform addresses (scalar loads: it fits the scalar registers). For
-  // G >= 2 it would not, so it is spread over vector registers instead:
-  // word w sits in register w / 16 of lane w % 16 of every 16-lane row, and
-  // each dot product fetches it with a row broadcast (dot_chunk2/4/8).
-  constexpr bool kBcastQ = G >= 2;
-  constexpr int QR = kBcastQ ? G * D / 32 : 1;
+  // Query words of this lane's half: half-local word w of head h (w < D/4)
+  // sits in register (h * D/4 + w) / 16 of lane w % 16 of every 16-lane row of
+  // that half, and each dot product fetches it with a row broadcast.
   uint32_t qd[QR];
   int qb = -1, qj = -1;  // (sequence, KV head) whose query qd holds
+  int par = 0;           // parity of the current item
 
   for (ItemRun run = first_item(a); run.left > 0 && run.b < a.B;) {
     const int b = run.b, j = run.j, p = run.p;
@@ -704,12 +811,19 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
       }
     }
 
-    const uint32_t* qw = reinterpret_cast<const uint32_t*>(q + ((size_t)b * H + (size_t)j * G) * D);
-    if (kBcastQ && (b != qb || j != qj)) {
+    if (b != qb || j != qj) {
+      const uint32_t* qw = reinterpret_cast<const uint32_t*>(q + ((size_t)b * H + (size_t)j * G) * D);
 #pragma unroll
-      for (int r = 0; r < QR; ++r) qd[r] = qw[16 * r + (threadIdx.x & 15)];
+      for (int r = 0; r < QR; ++r) {
+        const int wl = 16 * r + (lane & 15);
+        qd[r] = qw[(wl / WPH) * (D / 2) + hf * WPH + wl % WPH];
+      }
       qb = b;
       qj = j;
+      // Wait here, in a form the compiler's own wait counting sees: a query
+      // load still counted as pending inside the tile loop would make it wait
+      // for the K prefetch as well. (vmcnt(0); the other counters at maximum.)
+      __builtin_amdgcn_s_waitcnt(0x0F70);
     }
 
     float m[G], lpart[G], acc[G][8];
@@ -722,19 +836,16 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
     }
 
     // Buffer resources over this (sequence, KV head) slab, limited to the
-    // sequence's valid rows: a read at or past row n returns zeros, so the
-    // tail of the last tile needs no clamping and padding rows are never
-    // fetched. Byte offsets fit 32 bits (the host limits T_max * D * 2).
-    // A paged cache gets one pair of resources per tile instead (tile_rsrc).
+    // sequence's valid rows: a read at or past row n returns zeros. A paged
+    // cache gets one pair per tile (its 32 rows lie in one page: page_size is
+    // a multiple of 32 and tiles start at multiples of 32); a table entry
+    // outside [0, num_pages) reads as zeros.
     const size_t head_off = paged ? 0 : ((size_t)b * h_kv + j) * (size_t)T_max * D;
     const int valid_bytes = n * (D * 2);
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + head_off), 0, valid_bytes, kBufWord3);
     const __amdgpu_buffer_rsrc_t vrs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + head_off), 0, valid_bytes, kBufWord3);
-    // Paged: the 64 rows of a tile lie in one page (page_size is a multiple of
-    // 64 and tiles start at multiples of 64); its resources cover the tile's
-    // rows below n, and a table entry outside [0, num_pages) reads as zeros.
     auto tile_rsrc = [&](int t0, __amdgpu_buffer_rsrc_t& kr, __amdgpu_buffer_rsrc_t& vr_, uint32_t& toff) {
       if (!paged) {
         kr = krs;
@@ -744,14 +855,14 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
       }
       const int phys = a.block_table[(size_t)b * a.max_pages + (t0 >> a.page_shift)];
       const bool ok = phys >= 0 && phys < a.num_pages;
-      const int rows = ok ? min(kPoRows, n - t0) : 0;
+      const int rows = ok ? min(TR, n - t0) : 0;
       const size_t off = (((size_t)(ok ? phys : 0) * h_kv + j) * a.page_size + (t0 & (a.page_size - 1))) * D;
       kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + off), 0, rows * (D * 2), kBufWord3);
       vr_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + off), 0, rows * (D * 2), kBufWord3);
       toff = 0;
     };
 
-    for (int t0 = start + wave * kPoRows; t0 < end; t0 += kWaves * kPoRows) {
+    for (int t0 = start + wave * TR; t0 < end; t0 += kWaves * TR) {
       __amdgpu_buffer_rsrc_t krt, vrt;
       uint32_t toff;
       tile_rsrc(t0, krt, vrt, toff);
@@ -761,58 +872,44 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
       for (int i = 0; i < NV; ++i) vr[i] = load_v(vrt, toff, i);
       // The K copies were issued first: once at most NV memory operations of
       // this wave are outstanding, they have all landed.
-      if constexpr (NV == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-      else if constexpr (NV == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if constexpr (NV == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
 
-      // ---- scores: lane owns position t0 + lane; its K row comes out of LDS
-      // in one batch, then G dot products run on it.
-      const unsigned char* krow = kt + lane * (D * 2);
+      // ---- scores: lane (hf, pr) dots half hf of position t0 + pr.
+      const unsigned char* krow = &ktile[wave][0] + pr * (D * 2);
       float s[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) s[h] = 0.f;
-      // The row is read from LDS in KS slices of CH / KS chunks, each used at
-      // once, so only one slice is held in registers beside the V tile.
-      constexpr int KS = G >= 4 ? 2 : 1;
-      constexpr int CS = CH / KS;
+      constexpr int KS = (G >= 4 && HC >= 8) ? 2 : 1;
+      constexpr int CS = HC / KS;
       static_for<KS>([&](auto ks_) {
         constexpr int ks = decltype(ks_)::value;
         uint4 kk[CS];
 #pragma unroll
         for (int u = 0; u < CS; ++u)
-          kk[u] = *reinterpret_cast<const uint4*>(krow + 16 * ((ks * CS + u) ^ (lane % CH)));
+          kk[u] = *reinterpret_cast<const uint4*>(krow + 16 * ((hf * HC + ks * CS + u) ^ (pr % CH)));
         static_for<CS>([&](auto u_) {
           constexpr int u = decltype(u_)::value;
-          constexpr int jc = ks * CS + u;
-          if constexpr (kBcastQ) {
-            // Query word h*D/2 + 4*jc + e is register (h*D/2 + 4*jc) / 16,
-            // row lane 4*(jc % 4) + e.
-            constexpr int l0 = 4 * (jc % 4);
-            uint32_t qr[G];
+          constexpr int jc = ks * CS + u;        // chunk within the half
+          constexpr int l0 = 4 * (jc % 4);
+          uint32_t qr[G];
 #pragma unroll
-            for (int h = 0; h < G; ++h) qr[h] = qd[(h * (D / 2) + 4 * jc) / 16];
-            if constexpr (G == 2) dot_chunk2<l0>(s, qr, kk[u]);
-            else if constexpr (G == 4) dot_chunk4<l0>(s, qr, kk[u]);
-            else dot_chunk8<l0>(s, qr, kk[u]);
-          } else {
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-              const uint32_t* qh = qw + h * (D / 2) + 4 * jc;
-              float a = s[h];
-              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[0]), __builtin_bit_cast(bf16x2, kk[u].x), a, false);
-              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[1]), __builtin_bit_cast(bf16x2, kk[u].y), a, false);
-              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[2]), __builtin_bit_cast(bf16x2, kk[u].z), a, false);
-              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qh[3]), __builtin_bit_cast(bf16x2, kk[u].w), a, false);
-              s[h] = a;
-            }
-          }
+          for (int h = 0; h < G; ++h) qr[h] = qd[(h * WPH + 4 * jc) / 16];
+          if constexpr (G == 1) dot_chunk1<l0>(s, qr, kk[u]);
+          else if constexpr (G == 2) dot_chunk2<l0>(s, qr, kk[u]);
+          else if constexpr (G == 4) dot_chunk4<l0>(s, qr, kk[u]);
+          else dot_chunk8<l0>(s, qr, kk[u]);
         });
-        // Keep the next slice's reads below this slice's arithmetic.
         __builtin_amdgcn_sched_barrier(0);
       });
       // The K area is rewritten by the next tile's copy: all its reads are done.
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      const bool valid = t0 + lane < end;
+      if constexpr (G == 1) half_sum1(s);
+      else if constexpr (G == 2) half_sum2(s);
+      else if constexpr (G == 4) half_sum4(s);
+      else half_sum8(s);
+
+      const bool valid = t0 + pr < end;
       bool need = false;
       float mx[G];
 #pragma unroll
@@ -841,15 +938,18 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
           for (int e = 0; e < 8; ++e) acc[h][e] *= f;
         }
       }
+      // Both halves hold every score; the lanes of half 0 own the weights.
       float w[GP];
 #pragma unroll
       for (int h = 0; h < GP; ++h) {
         w[h] = (h < G && valid) ? fast_exp2(s[h < G ? h : 0] - m[h < G ? h : 0]) : 0.f;
-        if (h < G) lpart[h] += w[h];
+        if (h < G) lpart[h] += hf ? 0.f : w[h];
       }
+      if (hf == 0) {
 #pragma unroll
-      for (int h = 0; h < GP; h += 4)
-        *reinterpret_cast<float4*>(wt + lane * GP + h) = make_float4(w[h], w[h + 1], w[h + 2], w[h + 3]);
+        for (int h = 0; h < GP; h += 4)
+          *reinterpret_cast<float4*>(wt + pr * GP + h) = make_float4(w[h], w[h + 1], w[h + 2], w[h + 3]);
+      }
 
       // ---- output: lane (rr, c) accumulates rows i*RPI + rr, dims 8c .. 8c+7
 #pragma unroll
@@ -874,52 +974,52 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
       }
     }
 
-    // All lanes of a wave share m: the row groups add up, the per-position sums add up.
+    // All lanes of a wave share m: the row groups add up (lane swaps, no
+    // LDS), the per-position sums add up.
     float L[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       L[h] = wave_sum(lpart[h]);
 #pragma unroll
-      for (int off = LPR; off < 64; off <<= 1)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, 64);
+      for (int e = 0; e < 8; ++e) {
+        float x = acc[h][e];
+        if constexpr (LPR == 8) x += __shfl_xor(x, 8, 64);
+        acc[h][e] = xor32_sum(xor16_sum(x));
+      }
     }
 
-    // Combine the waves through LDS and write this partition's partial. The
-    // per-wave sums reuse the K tile area once every wave has left its loop.
-    static_assert(sizeof(float) * kWaves * G * D <= sizeof(ktile), "combine area too small");
-    __syncthreads();
-    float (*sm_acc)[G][D] = reinterpret_cast<float (*)[G][D]>(&ktile[0][0]);
+    // Combine the waves through LDS and write this partition's partial.
     if (lane < LPR) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sm_acc[wave][h][c * 8 + e] = acc[h][e];
+        float4* dst = reinterpret_cast<float4*>(&comb[par][wave][h][c * 8]);
+        dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+        dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
         if (c == 0) {
-          sm_m[wave][h] = m[h];
-          sm_l[wave][h] = L[h];
+          sm_m[par][wave][h] = m[h];
+          sm_l[par][wave][h] = L[h];
         }
       }
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
       const int h = idx / D, d = idx % D;
-      float M = sm_m[0][h];
+      float M = sm_m[par][0][h];
 #pragma unroll
-      for (int w2 = 1; w2 < kWaves; ++w2) M = fmaxf(M, sm_m[w2][h]);
+      for (int w2 = 1; w2 < kWaves; ++w2) M = fmaxf(M, sm_m[par][w2][h]);
       float Ls = 0.f, A = 0.f;
 #pragma unroll
       for (int w2 = 0; w2 < kWaves; ++w2) {
-        const float mw = sm_m[w2][h];
+        const float mw = sm_m[par][w2][h];
         const float f = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
-        Ls += sm_l[w2][h] * f;
-        A += sm_acc[w2][h][d] * f;
+        Ls += sm_l[par][w2][h] * f;
+        A += comb[par][w2][h][d] * f;
       }
       const size_t row = ((size_t)b * H + (size_t)j * G + h) * NP + p;
       part_out[row * D + d] = A / Ls;
       if (d == 0) part_lse[row] = M + fast_log2(Ls);
     }
-    __syncthreads();  // the combine area is the next item's K tile area
+    par ^= 1;
     if (--run.left > 0) next_item(run, a);
   }
 }
@@ -941,10 +1041,12 @@ int device_cus() {
 // share of the non-empty partitions.
 template <int D, int G>
 hipError_t launch_po(const GqaArgs& a, hipStream_t stream) {
+  constexpr auto kernel = &gqa_partial_po_kernel<D, G>;
   static const int per_cu = [] {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&gqa_partial_po_kernel<D, G>),
-                                                     kThreads, 0) != hipSuccess || nb < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(kernel), kThreads, 0) !=
+            hipSuccess ||
+        nb < 1)
       nb = 1;
     return nb;
   }();
@@ -952,7 +1054,7 @@ hipError_t launch_po(const GqaArgs& a, hipStream_t stream) {
   if (cus <= 0) return hipErrorInvalidDevice;
   const long long items = (long long)a.B * a.h_kv * a.NP;
   const int grid = (int)std::min<long long>(items, (long long)cus * per_cu);
-  hipLaunchKernelGGL((gqa_partial_po_kernel<D, G>), dim3(grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -967,11 +1069,10 @@ hipError_t launch_one(const GqaArgs& a, hipStream_t stream) {
 #endif
 // Smallest group size served by the position-per-lane kernel (bf16 only).
 constexpr int kPoMinGroup = ATTN_PO_MIN_GROUP;
-
 template <class E, int D>
 hipError_t launch_d(int G, const GqaArgs& a, hipStream_t s) {
   if constexpr (sizeof(typename E::storage) == 2) {
-    // The position-per-lane kernel reads a paged cache one 64-row tile at a time.
+    // The position-per-lane kernel reads a paged cache one 32-row tile at a time.
     const bool tiles_fit = a.block_table == nullptr || a.page_size % kPoRows == 0;
     if (G >= kPoMinGroup && tiles_fit) {
       switch (G) {

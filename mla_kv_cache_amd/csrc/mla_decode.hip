@@ -11,18 +11,18 @@
 //   O^T [512 dims x 32 heads]     += L_tile^T [512 x 32] . P^T [32 x 32]
 //
 // One work-group owns (sequence b, head block of up to 128 heads, partition
-// p) and runs two waves per 32 heads (8 waves for 128 heads, two per SIMD).
-// The two waves of a pair split the 576-wide score contraction in halves,
-// exchange their fp32 partial scores through LDS and add them in a fixed
-// order (both then hold the same scores and the same softmax state), and
-// split the 512 output dims in halves. Per wave that leaves 18 query
-// fragments and 8 output tiles resident in registers for the partition.
+// p) and runs one wave per 32 heads (four for 128 heads, one per SIMD). Each
+// wave does the whole 576-wide score contraction and all 512 output dims for
+// its heads, so waves never exchange scores; they meet once per tile, to
+// recycle the tile buffers. A wave holds its 36 query fragments (144 VGPRs)
+// and 16 output tiles (256 AGPRs) for the whole partition.
 //
-// The latent tile (32 positions x 576, padded to a 1168-byte row stride so
-// that both read patterns below are free of bank conflicts) is copied from
-// HBM straight into LDS with global_load_lds (no register staging), double
-// buffered: the copy of tile i+1 is in flight while tile i is computed. HBM
-// sees every cached row of the partition once.
+// The latent tile (32 positions x 576) is copied from HBM straight into LDS
+// with global_load_lds (no register staging) into a ring of three buffers:
+// the copies of the next two tiles are in flight while one is computed. HBM
+// sees every cached row of the partition once. Rows are 1152 bytes with
+// 16-byte chunks XOR-swizzled per row, which keeps both read patterns below
+// free of bank conflicts on the 64-bank LDS.
 //
 // MFMA 32x32x16 bf16 operand layout (lane l): A[m][k] holds m = l % 32,
 // k = 8*(l/32) + j; B[k][n] holds n = l % 32, k = 8*(l/32) + j; result
@@ -39,9 +39,9 @@
 //
 // The weights enter the second product as a pair of bf16 values hi + lo
 // (two MFMAs on the same latent fragment), so they carry about 16 significant
-// bits instead of bf16's 8; accumulation is fp32 throughout. Online softmax in the exp2 domain with the same lazy
-// rescale rule as the GQA kernel (only when a tile's maximum exceeds the
-// running one by more than 8).
+// bits instead of bf16's 8; accumulation is fp32 throughout. Online softmax in
+// the exp2 domain with the same lazy rescale rule as the GQA kernel (only when
+// a tile's maximum exceeds the running one by more than 8).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -61,7 +61,6 @@ constexpr int kDc = 512;
 constexpr int kDr = 64;
 constexpr int kRow = kDc + kDr;            // 576 bf16 per cached token
 constexpr int kTile = 32;                  // positions per tile
-constexpr int kStride = kRow + 8;          // LDS row stride in bf16 (1168 bytes)
 constexpr int kSteps = kRow / 16;          // 36 k-steps of the score product
 constexpr int kOTiles = kDc / 32;          // 16 output tiles of 32 latent dims
 constexpr float kTau = 8.0f;
@@ -83,8 +82,17 @@ __device__ __forceinline__ float partner_half(float v) {
   return (threadIdx.x & 32) ? a : b;
 }
 
-constexpr int kRowChunks = kStride / 8;               // 73 16-byte chunks per LDS row (72 + pad)
-constexpr int kTileBlocks = (kTile * kStride * 2 + 1023) / 1024;  // 37 1 KiB blocks hold a tile
+// Tile layout in LDS: rows of 72 16-byte chunks (1152 bytes, no padding),
+// logical chunk c of row r stored at chunk c ^ sw(r), with sw(r) the
+// bit-reversed value of (r / 2) % 8. On the 64-bank LDS this spreads both
+// read patterns: the score reads (one chunk of each of 32 rows) and the
+// transposed output reads (64 bytes of each of 4 rows per half-wave).
+__device__ __forceinline__ int tile_sw(int r) {
+  const int x = (r >> 1) & 7;
+  return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
+}
+constexpr int kRowChunks = kRow / 8;                     // 72
+constexpr int kTileBlocks = kTile * kRowChunks / 64;     // 36 blocks of 1 KiB
 
 // Copy blocks per tile for a work-group of NWAVES waves: rounded up so every
 // wave issues the same number of copies (the extra blocks land in slack space
@@ -95,20 +103,18 @@ struct TileCopy {
   static constexpr int kBlocks = kPerWave * NWAVES;
   static constexpr int kBufBytes = kBlocks * 1024;
 };
-constexpr int kHalfSteps = kSteps / 2;                   // 18 score k-steps per wave
-constexpr int kHalfTiles = kOTiles / 2;                  // 8 output tiles per wave
 
 // Copy one latent tile (positions [t0, t0+32), rows past `end` replaced by row
-// end-1) into an LDS buffer. Each wave copies whole 1 KiB blocks: lane i of
-// block k fills LDS chunk 64k + i; pad chunks and the slack past the tile
-// receive a harmless in-bounds row.
+// end-1) into an LDS buffer. Lane i of block k fills LDS chunk 64k + i =
+// (row, pc) and fetches logical chunk pc ^ sw(row) of that row; slack blocks
+// past the tile receive a harmless in-bounds row.
 //
 // The copy is issued as global_load_lds_dwordx4 in inline assembly: it writes
 // no register, only LDS, and M0 holds the block's LDS address (no other code
 // in these kernels uses M0). Written this way the compiler does not insert a
 // wait for the copy before every later LDS read (it cannot prove that the
-// reads touch the other buffer); the kernel waits for the copy itself
-// (s_waitcnt vmcnt(0) before the barrier that opens the next tile).
+// reads touch another buffer); the kernel waits for the copy itself
+// (s_waitcnt vmcnt before the barrier that opens the tile).
 // Row r of the tile is read at base + (r - base_row) * 576: for a contiguous
 // cache base is the sequence's first row and base_row = 0; for a paged cache
 // base is the page row that holds t0, base_row = t0 (the tile lies inside one
@@ -121,34 +127,68 @@ __device__ __forceinline__ void copy_tile(unsigned char* buf, const uint16_t* ba
   for (int k = 0; k < TileCopy<NWAVES>::kPerWave; ++k) {
     const int blk = wave + NWAVES * k;
     const int ci = 64 * blk + lane;
-    const int row = ci / kRowChunks, c16 = ci % kRowChunks;
-    const bool data = row < kTile && c16 < kRow / 8;
+    const int row = ci / kRowChunks, pc = ci % kRowChunks;
+    const bool data = row < kTile;
+    const int lc = data ? pc ^ tile_sw(row) : 0;
     const int grow = min(t0 + (data ? row : 0), end - 1);
-    const uint16_t* src = base + (size_t)(grow - base_row) * kRow + (data ? c16 * 8 : 0);
+    const uint16_t* src = base + (size_t)(grow - base_row) * kRow + lc * 8;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + 1024u * (uint32_t)blk);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "memory");
   }
 }
 
 // Wait until this wave's copies of the current tile have landed while the
-// copies of the next tile (kPerWave of them, issued later) may still be in
-// flight, then barrier: afterwards every wave's copies of the current tile
-// are in LDS and every wave is done with the tile before it.
+// copies of the next tile (N of them, issued later) may still be in flight,
+// then barrier: afterwards every wave's copies of the current tile are in
+// LDS and every wave is done with the tile before it.
 template <int N>
 __device__ __forceinline__ void wait_tile_barrier(bool next_in_flight) {
   if (next_in_flight) {
-    if constexpr (N == 19) asm volatile("s_waitcnt vmcnt(19) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (N == 7) asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else static_assert(N == 5, "no wait defined for this copy count");
+    if constexpr (N == 36) asm volatile("s_waitcnt vmcnt(36) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else static_assert(N == 9, "no wait defined for this copy count");
   } else {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 }
 
-template <int NHB, bool PAGED>
-__global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(const MlaArgs a) {
+// acc *= f on an accumulator tile that lives in AGPRs, in place, through one
+// temporary VGPR. Written as assembly because the compiler, asked for a
+// vector multiply of the whole tile, keeps VGPR copies of all 16 tiles and
+// spills; the caller waits out the matrix-core write latency first.
+__device__ __forceinline__ void scale_acc(f32x16& acc, float f) {
+  float e[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) e[r] = acc[r];
+  float t;
+#pragma unroll
+  for (int r = 0; r < 16; r += 4)
+    asm volatile(
+        "v_accvgpr_read_b32 %4, %0\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %0, %4\n\t"
+        "v_accvgpr_read_b32 %4, %1\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %1, %4\n\t"
+        "v_accvgpr_read_b32 %4, %2\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %2, %4\n\t"
+        "v_accvgpr_read_b32 %4, %3\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %3, %4\n\t"
+        "s_nop 1"
+        : "+a"(e[r]), "+a"(e[r + 1]), "+a"(e[r + 2]), "+a"(e[r + 3]), "=&v"(t) : "v"(f));
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = e[r];
+}
+
+// Read-ahead depths of the two products (operand reads issued before the
+// products that consume them; limited by the registers left beside the query
+// fragments and the accumulators).
+constexpr int kQkAhead = 6;
+constexpr int kPvAhead = 3;
+
+// One wave per 32 heads, each with the whole 576-wide score contraction and
+// all 512 output dims (see the file comment). NW waves (NW * 32 heads) share
+// each latent tile; the kernel runs one wave per SIMD, and the matrix cores
+// are kept busy by operand reads issued ahead of the products.
+template <int NW, bool PAGED>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_partial_kernel(const MlaArgs a) {
   const uint16_t* __restrict__ q_nope = static_cast<const uint16_t*>(a.q_nope);
   const uint16_t* __restrict__ q_rope = static_cast<const uint16_t*>(a.q_rope);
   // Not restrict: a decode step writes one row of the cache before reading.
@@ -157,15 +197,8 @@ __global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(const MlaArgs
   float* __restrict__ part_lse = a.part_lse;
   const int H = a.H, T_max = a.T_max, P = a.P, NP = a.NP;
   const float qk_scale_log2 = a.qk_scale_log2;
-  constexpr int NWAVES = 2 * NHB;
-  // Three tile buffers as separate objects: the copies of the next two tiles
-  // are in flight while one is computed, and the compiler can tell the copy
-  // into one buffer from the reads of another.
-  using TC = TileCopy<NWAVES>;
-  __shared__ __attribute__((aligned(1024))) unsigned char buf0[TC::kBufBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char buf1[TC::kBufBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char buf2[TC::kBufBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char xbuf[NWAVES * 4096];
+  using TC = TileCopy<NW>;
+  __shared__ __attribute__((aligned(1024))) unsigned char bufs[3][TC::kBufBytes];
 
   const int p = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;
   const int len0 = a.seq_lens[b];
@@ -180,84 +213,90 @@ __global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(const MlaArgs
                                     static_cast<const uint16_t*>(a.lat_new) + (size_t)b * kRow);
   }
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int kh = wave & 1;             // half of the contraction / of the output dims
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;          // which 16 of a tile's 32 positions this lane holds
-  const int col = lane & 31;           // this lane's head within the pair's 32
-  const int head = hb * (32 * NHB) + (wave >> 1) * 32 + col;
+  const int col = lane & 31;           // this lane's head within the wave's 32
+  const int head = hb * (32 * NW) + wave * 32 + col;
 
-  // Query fragments for this wave's half of the 576 score dims.
-  uint4 qf[kHalfSteps];
+  // Query fragments for all 576 score dims.
+  uint4 qf[kSteps];
   {
     const uint16_t* qn = q_nope + ((size_t)b * H + head) * kDc;
     const uint16_t* qr = q_rope + ((size_t)b * H + head) * kDr;
 #pragma unroll
-    for (int ks = 0; ks < kHalfSteps; ++ks) {
-      const int d = 16 * (kHalfSteps * kh + ks) + 8 * half;
+    for (int ks = 0; ks < kSteps; ++ks) {
+      const int d = 16 * ks + 8 * half;
       qf[ks] = d < kDc ? ld16(qn + d) : ld16(qr + (d - kDc));
     }
+    // Wait for the query here, in a form the compiler's own wait counting
+    // sees (vmcnt(0), the other counters at maximum): otherwise it waits for
+    // them inside the tile loop with counts that also cover the tile copies
+    // in flight, which would stall every tile on its successors' copies.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 
-  f32x16 acc[kHalfTiles];
+  f32x16 acc[kOTiles];
 #pragma unroll
-  for (int t = 0; t < kHalfTiles; ++t)
+  for (int t = 0; t < kOTiles; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
   float m = kNegInf, lsum = 0.f;
 
   const uint16_t* lat_b = lat + (PAGED ? 0 : (size_t)b * T_max * kRow);
-  // Paged: the page row that holds row t0 (page_size is a multiple of the
-  // tile, tiles start at multiples of it); a table entry outside
-  // [0, num_pages) is clamped into range (values unspecified, never a fault).
   auto page_base = [&](int t0) -> const uint16_t* {
     const int phys = min(max(a.block_table[(size_t)b * a.max_pages + (t0 >> a.page_shift)], 0),
                          a.num_pages - 1);
     return lat + ((size_t)phys * a.page_size + (t0 & (a.page_size - 1))) * kRow;
   };
   auto copy = [&](unsigned char* buf, int t0) {
-    if constexpr (PAGED) copy_tile<NWAVES>(buf, page_base(t0), t0, t0, end, wave, lane);
-    else copy_tile<NWAVES>(buf, lat_b, 0, t0, end, wave, lane);
+    const uint16_t* base = PAGED ? page_base(t0) : lat_b;
+    const int base_row = PAGED ? t0 : 0;
+    copy_tile<NW>(buf, base, base_row, t0, end, wave, lane);
   };
-  // LDS transpose-read addressing, constant per lane (see the file comment).
   const int g16 = lane >> 4, i16 = lane & 15;
   const int tr_row = 4 * (g16 >> 1) + (i16 >> 2);
-  const int tr_col = 256 * kh + 16 * (g16 & 1) + 4 * (i16 & 3);
+  const int tr_col = 16 * (g16 & 1) + 4 * (i16 & 3);
+  // Swizzle offsets (bf16 units) that depend on the lane only. The score read
+  // of step ks takes qoff[ks % 4]; the output read of tile t and row half h
+  // (rows + 8h) takes poff[h][t % 2]. Rows 16ks + tr_row + 8h have the same
+  // swizzle for both ks.
+  int qoff[4], poff[2][2];
+#pragma unroll
+  for (int k3 = 0; k3 < 4; ++k3) qoff[k3] = 8 * ((2 * k3 + half) ^ tile_sw(col));
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int t1 = 0; t1 < 2; ++t1)
+      poff[h][t1] = 8 * ((4 * t1 + (tr_col >> 3)) ^ tile_sw(8 * h + tr_row)) + (tr_col & 7);
 
-  // One tile: wait for its copy, start the copy of the tile after next into
-  // the third buffer, then scores, exchange, softmax and the output product.
   auto tile = [&](const unsigned char* __restrict__ cur_b, unsigned char* __restrict__ nxt_b, int t0) {
     const uint16_t* cur = reinterpret_cast<const uint16_t*>(cur_b);
     wait_tile_barrier<TC::kPerWave>(t0 + kTile < end);
     if (t0 + 2 * kTile < end) copy(nxt_b, t0 + 2 * kTile);
 
-    // ---- partial scores over this wave's 288 dims: S^T = L . Q^T
+    // ---- scores S^T = L . Q^T over all 576 dims
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    const uint16_t* arow = cur + col * kStride + 16 * kHalfSteps * kh + 8 * half;
+    const uint16_t* arow = cur + col * kRow;
+    // The operand reads run kQkAhead steps ahead of the products that use
+    // them: the schedule below asks for reads, then one product per read.
 #pragma unroll
-    for (int ks = 0; ks < kHalfSteps; ++ks) {
-      const uint4 a = *reinterpret_cast<const uint4*>(arow + 16 * ks);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+    for (int ks = 0; ks < kSteps; ++ks) {
+      // chunk 2ks + half of row col sits at 8 * (ks / 4) + qoff[ks % 4]
+      const uint4 av = *reinterpret_cast<const uint4*>(arow + 64 * (ks >> 2) + qoff[ks & 3]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
                                                    __builtin_bit_cast(bf16x8, qf[ks]), s, 0, 0, 0);
     }
-    // ---- exchange with the partner wave; add in the fixed order (half 0) + (half 1)
-    {
-      float4* mine = reinterpret_cast<float4*>(xbuf + wave * 4096) + lane;
+    __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) mine[64 * g] = make_float4(s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]);
-      // LDS writes done, then a plain barrier: no release fence, which would
-      // also wait for the copy of the next tile that is in flight.
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      const float4* other = reinterpret_cast<const float4*>(xbuf + (wave ^ 1) * 4096) + lane;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 o = other[64 * g];
-        const float ov[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[4 * g + e] = kh == 0 ? s[4 * g + e] + ov[e] : ov[e] + s[4 * g + e];
-      }
+    for (int i = 0; i < kSteps - kQkAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, kQkAhead, 0);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- online softmax for head `col` over this tile's positions
     float x[16];
@@ -277,21 +316,17 @@ __global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(const MlaArgs
       }
     }
     mt = fmaxf(mt, partner_half(mt));
-    // The first tile always sets m (its first position is valid), so m is finite
-    // below and exp2(x - m) is 0 for masked positions without a select.
     const bool need = mt > m + kTau;
     if (__any(need)) {
       const float f = need ? fast_exp2(m - mt) : 1.f;
       m = need ? mt : m;
       lsum *= f;
+      // Matrix-core results are read back only after the wait states the
+      // hardware requires (this path is rare; see scale_acc).
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-      for (int t = 0; t < kHalfTiles; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[t][r] *= f;
+      for (int t = 0; t < kOTiles; ++t) scale_acc(acc[t], f);
     }
-    // Weights as a bf16 pair hi + lo (hi = bf16(p), lo = bf16(p - hi)): the
-    // product below runs once per part on the same latent fragment, so the
-    // weights enter with ~2^-17 relative error instead of bf16's 2^-9.
     uint32_t ph[8], pl[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
@@ -302,46 +337,59 @@ __global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(const MlaArgs
       pl[r >> 1] = pack_bf16x2(p0 - bf16_lo(h), p1 - bf16_hi(h));
     }
 
-    // ---- O^T += L^T . P^T over this wave's 256 output dims (two k-steps of 16 positions)
+    // ---- O^T += L^T . P^T over all 512 output dims (two k-steps of 16 positions)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8 pbh = __builtin_bit_cast(bf16x8, make_uint4(ph[4 * ks], ph[4 * ks + 1], ph[4 * ks + 2], ph[4 * ks + 3]));
       const bf16x8 pbl = __builtin_bit_cast(bf16x8, make_uint4(pl[4 * ks], pl[4 * ks + 1], pl[4 * ks + 2], pl[4 * ks + 3]));
-      const uint16_t* base = cur + (16 * ks + tr_row) * kStride + tr_col;
+      const uint16_t* base = cur + (16 * ks + tr_row) * kRow;
+      const uint16_t* base_hi = base + 8 * kRow;
 #pragma unroll
-      for (int t = 0; t < kHalfTiles; ++t) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 32 * t));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * kStride + 32 * t));
-        uint4 a;
-        a.x = __builtin_bit_cast(uint2, lo).x;
-        a.y = __builtin_bit_cast(uint2, lo).y;
-        a.z = __builtin_bit_cast(uint2, hi).x;
-        a.w = __builtin_bit_cast(uint2, hi).y;
-        const bf16x8 av = __builtin_bit_cast(bf16x8, a);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbh, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pbl, acc[t], 0, 0, 0);
+      for (int t = 0; t < kOTiles; ++t) {
+        // chunk 4t + tr_col / 8 of the row sits at 8 * (t / 2) + poff[.][t % 2]
+        const uint16_t* plo = base + 64 * (t >> 1) + poff[0][t & 1];
+        const uint16_t* phi = base_hi + 64 * (t >> 1) + poff[1][t & 1];
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)plo);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)phi);
+        uint4 av;
+        av.x = __builtin_bit_cast(uint2, lo).x;
+        av.y = __builtin_bit_cast(uint2, lo).y;
+        av.z = __builtin_bit_cast(uint2, hi).x;
+        av.w = __builtin_bit_cast(uint2, hi).y;
+        const bf16x8 aw = __builtin_bit_cast(bf16x8, av);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, pbh, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, pbl, acc[t], 0, 0, 0);
       }
+      // The operand reads of kPvAhead output tiles run ahead of the products.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvAhead, 0);
+#pragma unroll
+      for (int i = 0; i < kOTiles - kPvAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kPvAhead, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  copy(buf0, start);
-  if (start + kTile < end) copy(buf1, start + kTile);
-  for (int t0 = start;;) {
-    tile(buf0, buf2, t0);
-    if ((t0 += kTile) >= end) break;
-    tile(buf1, buf0, t0);
-    if ((t0 += kTile) >= end) break;
-    tile(buf2, buf1, t0);
-    if ((t0 += kTile) >= end) break;
+  // Tile i sits in buffer i % 3; the copy of tile i + 2 goes into the buffer
+  // of tile i - 1, which every wave has finished with at tile i's barrier.
+  copy(bufs[0], start);
+  if (start + kTile < end) copy(bufs[1], start + kTile);
+  int cur = 0;
+  for (int t0 = start; t0 < end; t0 += kTile) {
+    const int nxt = cur == 0 ? 2 : cur - 1;
+    tile(bufs[cur], bufs[nxt], t0);
+    cur = cur == 2 ? 0 : cur + 1;
   }
 
   // Lanes l and l^32 share a head and a running maximum; add their sums.
   lsum += partner_half(lsum);
   const float inv = 1.f / lsum;
   const size_t prow = ((size_t)b * H + head) * NP + p;
-  float* po = part_out + prow * kDc + 256 * kh;
+  float* po = part_out + prow * kDc;
 #pragma unroll
-  for (int t = 0; t < kHalfTiles; ++t) {
+  for (int t = 0; t < kOTiles; ++t) {
 #pragma unroll
     for (int r = 0; r < 16; r += 4) {
       const int d = 32 * t + 8 * (r >> 2) + 4 * half;
@@ -349,7 +397,7 @@ __global__ __launch_bounds__(128 * NHB, 1) void mla_partial_kernel(const MlaArgs
           make_float4(acc[t][r] * inv, acc[t][r + 1] * inv, acc[t][r + 2] * inv, acc[t][r + 3] * inv);
     }
   }
-  if (kh == 0 && half == 0) part_lse[prow] = m + fast_log2(lsum);
+  if (half == 0) part_lse[prow] = m + fast_log2(lsum);
 }
 
 }  // namespace
@@ -358,15 +406,16 @@ bool mla_supported(int H, int d_c, int d_r) {
   return d_c == kDc && d_r == kDr && H >= 32 && H % 32 == 0 && (H <= 128 || H % 128 == 0);
 }
 
+
 template <bool PAGED>
 hipError_t launch_mla_nhb(const MlaArgs& a, hipStream_t stream) {
-  const int nhb = a.H >= 128 ? 4 : a.H / 32;  // 32-head blocks per work-group
+  const int nhb = a.H >= 128 ? 4 : a.H / 32;  // 32-head blocks (waves) per work-group
   const dim3 grid(a.NP, a.H / (32 * nhb), a.B);
   switch (nhb) {
-    case 4: hipLaunchKernelGGL((mla_partial_kernel<4, PAGED>), grid, dim3(512), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((mla_partial_kernel<3, PAGED>), grid, dim3(384), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((mla_partial_kernel<2, PAGED>), grid, dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL((mla_partial_kernel<1, PAGED>), grid, dim3(128), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((mla_partial_kernel<4, PAGED>), grid, dim3(256), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((mla_partial_kernel<3, PAGED>), grid, dim3(192), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((mla_partial_kernel<2, PAGED>), grid, dim3(128), 0, stream, a); break;
+    default: hipLaunchKernelGGL((mla_partial_kernel<1, PAGED>), grid, dim3(64), 0, stream, a); break;
   }
   return hipGetLastError();
 }

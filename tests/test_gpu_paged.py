@@ -5,9 +5,9 @@ random permutation of physical slots; unused pages hold NaN and table
 entries past a sequence's last page hold garbage indices, so any read of
 them shows. The paged kernels run the same arithmetic as the contiguous ones
 on the same positions in the same order, so their output must equal the
-library's contiguous decode bit for bit (except bf16 pages of 16 or 32 rows,
-which take the per-row kernel); it must also match the oracle within the
-decode tolerances. Appends into pages are byte work and compared exactly.
+library's contiguous decode bit for bit (except bf16 pages of 16 rows, which
+take the per-row kernel); it must also match the oracle within the decode
+tolerances. Appends into pages are byte work and compared exactly.
 """
 
 import numpy as np
@@ -65,7 +65,8 @@ CASES = [
     (2, 32, 2, 128, 10, 64, torch.bfloat16, [640, 0]),
     (2, 16, 4, 64, 12, 64, torch.bfloat16, [700, 65]),
     (2, 8, 2, 128, 32, 16, torch.bfloat16, [500, 17]),          # small pages: per-row gather
-    (2, 8, 2, 128, 16, 32, torch.bfloat16, [512, 33]),
+    (2, 8, 2, 128, 16, 32, torch.bfloat16, [512, 33]),          # one tile per page
+    (3, 32, 4, 64, 24, 32, torch.bfloat16, [700, 33, 768]),
     (2, 16, 4, 128, 8, 64, torch.float32, [512, 200]),
     (2, 16, 8, 64, 20, 16, torch.float32, [320, 100]),
 ]
@@ -82,9 +83,9 @@ def test_paged_matches_contiguous_and_oracle(gpu, case):
     vp, _ = _paginate_kv(v, lens, ps, 1)
     out = m.attn_decode_gqa_paged(q.to(gpu), kp.to(gpu), vp.to(gpu), table.to(gpu), l.to(gpu), scale=w.scale)
     lin = m.attn_decode_gqa(q.to(gpu), k.to(gpu), v.to(gpu), l.to(gpu), scale=w.scale)
-    # bf16 pages shorter than a 64-row tile take the per-row kernel, whose
+    # bf16 pages shorter than a 32-row tile take the per-row kernel, whose
     # reduction order differs from the contiguous bf16 kernel's: tolerance only
-    same_kernel = dt == torch.float32 or h_q // h_kv == 16 or ps % 64 == 0
+    same_kernel = dt == torch.float32 or h_q // h_kv == 16 or ps % 32 == 0
     if same_kernel:
         assert torch.equal(_bits(out), _bits(lin))
     ref = oracle.decode_gqa_paged(q, kp, vp, table, l, w.scale, ps)

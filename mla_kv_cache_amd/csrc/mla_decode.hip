@@ -200,7 +200,24 @@ void mla_partial_kernel(const MlaArgs a) {
   using TC = TileCopy<NW>;
   __shared__ __attribute__((aligned(1024))) unsigned char bufs[3][TC::kBufBytes];
 
-  const int p = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;
+  // Work-group L of the 1-D grid serves (partition p, head block hb,
+  // sequence b). Work-groups are handed to the 8 XCDs in turn (L % 8), each
+  // with its own L2; when the grid allows, the NP partitions of one
+  // (sequence, head block) get consecutive slots of one XCD, so the query
+  // block they all read comes from that L2 after the first read.
+  const int L = blockIdx.x, NHBK = H / (32 * NW);
+  int p, hb, b;
+  if (gridDim.x % (8 * NP) == 0) {
+    const int x = L % 8, slot = L / 8;
+    const int g = (slot / NP) * 8 + x;
+    p = slot % NP;
+    hb = g % NHBK;
+    b = g / NHBK;
+  } else {
+    p = L % NP;
+    hb = (L / NP) % NHBK;
+    b = L / (NP * NHBK);
+  }
   const int len0 = a.seq_lens[b];
   const int n = attended_len(len0, a.lat_new ? 1 : 0, T_max);
   const int start = p * P;
@@ -410,7 +427,9 @@ bool mla_supported(int H, int d_c, int d_r) {
 template <bool PAGED>
 hipError_t launch_mla_nhb(const MlaArgs& a, hipStream_t stream) {
   const int nhb = a.H >= 128 ? 4 : a.H / 32;  // 32-head blocks (waves) per work-group
-  const dim3 grid(a.NP, a.H / (32 * nhb), a.B);
+  const long long groups = (long long)a.NP * (a.H / (32 * nhb)) * a.B;
+  if (groups > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)groups);
   switch (nhb) {
     case 4: hipLaunchKernelGGL((mla_partial_kernel<4, PAGED>), grid, dim3(256), 0, stream, a); break;
     case 3: hipLaunchKernelGGL((mla_partial_kernel<3, PAGED>), grid, dim3(192), 0, stream, a); break;

@@ -212,3 +212,29 @@ def test_full_size_workload_sampled_rows(gpu, name):
     worst = _sampled_parity(W.NAMED[name])
     print(f"{name}: worst sampled max-abs error {worst:.3e}")
     assert worst <= 2e-3
+
+
+@pytest.mark.parametrize("B,h_q,h_kv,D", [(150, 8, 2, 64), (100, 64, 8, 128), (70, 16, 16, 128)])
+def test_persistent_split_many_sequences(gpu, B, h_q, h_kv, D):
+    """The bf16 kernel splits the non-empty (sequence, KV head, partition) items
+    evenly over its resident work-groups, scanning the lengths 64 sequences at
+    a time. More than 64 sequences, empty, one-position and full rows mixed
+    in: every row gets exactly its own partitions, for planned and explicit
+    partition sizes (including ones that do not divide the tile)."""
+    m = _m()
+    g = torch.Generator().manual_seed(21 + B)
+    T = 300
+    lens = torch.randint(0, T + 1, (B,), generator=g, dtype=torch.int32)
+    lens[::7] = 0
+    lens[3::11] = 1
+    lens[5::13] = T
+    w = W.small_gqa(B, h_q, h_kv, D, T, seed=22 + B)
+    (q, k, v, l), (gq, gk, gv, gl) = _inputs(w, gpu, lens)
+    ref = oracle.decode_gqa(q, k, v, l, w.scale)
+    out = m.attn_decode_gqa(gq, gk, gv, gl, scale=w.scale)
+    assert np.all(np.abs(_f64(out) - ref) <= 2e-3 + _half_ulp_bf16(ref))
+    for P in (32, 100, 512):
+        got = _f64(_run_fp32_out(m, gq, gk, gv, gl, P, w.scale))
+        assert float(np.abs(got - ref).max()) <= 2e-3, P
+    empty = (lens == 0).nonzero().flatten().tolist()
+    assert torch.equal(out[empty], torch.zeros_like(out[empty]))

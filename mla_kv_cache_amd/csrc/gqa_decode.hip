@@ -795,6 +795,32 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
   int qb = -1, qj = -1;  // (sequence, KV head) whose query qd holds
   int par = 0;           // parity of the current item
 
+  // Tile resources for (sequence bb, KV head jj, attended length nn), tile t0.
+  // Contiguous cache: the slab, limited to the sequence's valid rows (a read
+  // at or past row nn returns zeros). Paged cache: the tile's 32 rows, which
+  // lie in one page (page_size is a multiple of 32 and tiles start at
+  // multiples of 32); a table entry outside [0, num_pages) reads as zeros.
+  auto rsrc_at = [&](int bb, int jj, int nn, int t0, __amdgpu_buffer_rsrc_t& kr, __amdgpu_buffer_rsrc_t& vr_,
+                     uint32_t& toff) {
+    if (!paged) {
+      const size_t head_off = ((size_t)bb * h_kv + jj) * (size_t)T_max * D;
+      kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + head_off), 0, nn * (D * 2), kBufWord3);
+      vr_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + head_off), 0, nn * (D * 2), kBufWord3);
+      toff = (uint32_t)t0 * (D * 2);
+      return;
+    }
+    const int phys = a.block_table[(size_t)bb * a.max_pages + (t0 >> a.page_shift)];
+    const bool ok = phys >= 0 && phys < a.num_pages;
+    const int rows = ok ? min(TR, nn - t0) : 0;
+    const size_t off = (((size_t)(ok ? phys : 0) * h_kv + jj) * a.page_size + (t0 & (a.page_size - 1))) * D;
+    kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + off), 0, rows * (D * 2), kBufWord3);
+    vr_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + off), 0, rows * (D * 2), kBufWord3);
+    toff = 0;
+  };
+  // Whether this wave's first K tile of the current item was already
+  // requested before the previous item's combine.
+  bool k_ahead = false;
+
   for (ItemRun run = first_item(a); run.left > 0 && run.b < a.B;) {
     const int b = run.b, j = run.j, p = run.p;
     const int len0 = a.seq_lens[b];
@@ -835,38 +861,12 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
       for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     }
 
-    // Buffer resources over this (sequence, KV head) slab, limited to the
-    // sequence's valid rows: a read at or past row n returns zeros. A paged
-    // cache gets one pair per tile (its 32 rows lie in one page: page_size is
-    // a multiple of 32 and tiles start at multiples of 32); a table entry
-    // outside [0, num_pages) reads as zeros.
-    const size_t head_off = paged ? 0 : ((size_t)b * h_kv + j) * (size_t)T_max * D;
-    const int valid_bytes = n * (D * 2);
-    const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + head_off), 0, valid_bytes, kBufWord3);
-    const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + head_off), 0, valid_bytes, kBufWord3);
-    auto tile_rsrc = [&](int t0, __amdgpu_buffer_rsrc_t& kr, __amdgpu_buffer_rsrc_t& vr_, uint32_t& toff) {
-      if (!paged) {
-        kr = krs;
-        vr_ = vrs;
-        toff = (uint32_t)t0 * (D * 2);
-        return;
-      }
-      const int phys = a.block_table[(size_t)b * a.max_pages + (t0 >> a.page_shift)];
-      const bool ok = phys >= 0 && phys < a.num_pages;
-      const int rows = ok ? min(TR, n - t0) : 0;
-      const size_t off = (((size_t)(ok ? phys : 0) * h_kv + j) * a.page_size + (t0 & (a.page_size - 1))) * D;
-      kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + off), 0, rows * (D * 2), kBufWord3);
-      vr_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vc + off), 0, rows * (D * 2), kBufWord3);
-      toff = 0;
-    };
-
     for (int t0 = start + wave * TR; t0 < end; t0 += kWaves * TR) {
       __amdgpu_buffer_rsrc_t krt, vrt;
       uint32_t toff;
-      tile_rsrc(t0, krt, vrt, toff);
-      copy_k(krt, toff);
+      rsrc_at(b, j, n, t0, krt, vrt, toff);
+      if (!k_ahead) copy_k(krt, toff);
+      k_ahead = false;
       uint4 vr[NV];
 #pragma unroll
       for (int i = 0; i < NV; ++i) vr[i] = load_v(vrt, toff, i);
@@ -974,6 +974,28 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
       }
     }
 
+    // Request the K rows of this wave's first tile of the next item now, so
+    // the copy overlaps the combine below (not in a decode step, whose next
+    // item may first have to write its new row).
+    ItemRun nrun = run;
+    bool have_next = run.left > 1;
+    if (have_next) {
+      next_item(nrun, a);
+      have_next = nrun.b < a.B;
+    }
+    if (have_next && !a.k_new) {
+      const int nn = attended_len(a.seq_lens[nrun.b], 0, T_max);
+      const int nstart = window_lo(nn, a.window) + nrun.p * P;
+      const int nend = min(nstart, nn - P) + P;
+      if (nstart + wave * TR < nend) {
+        __amdgpu_buffer_rsrc_t krt, vrt;
+        uint32_t toff;
+        rsrc_at(nrun.b, nrun.j, nn, nstart + wave * TR, krt, vrt, toff);
+        copy_k(krt, toff);
+        k_ahead = true;
+      }
+    }
+
     // All lanes of a wave share m: the row groups add up (lane swaps, no
     // LDS), the per-position sums add up.
     float L[G];
@@ -1020,7 +1042,9 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
       if (d == 0) part_lse[row] = M + fast_log2(Ls);
     }
     par ^= 1;
-    if (--run.left > 0) next_item(run, a);
+    if (!have_next) break;
+    nrun.left = run.left - 1;
+    run = nrun;
   }
 }
 

@@ -28,6 +28,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
+// no swizzle, no stride): loads at or past num_records bytes return zeros.
+constexpr int kBufWord3 = 0x00020000;
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Data-parallel-primitive lane moves inside a 16-lane row.

@@ -624,10 +624,6 @@ __device__ __forceinline__ void half_sum8(float (&x)[8]) {
       : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]), "=&v"(t[7]));
 }
 
-// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
-// no swizzle, no stride): loads at or past num_records bytes return zeros.
-constexpr int kBufWord3 = 0x00020000;
-
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Work items of the persistent partial kernel: (sequence b, KV head j,

@@ -104,36 +104,39 @@ struct TileCopy {
   static constexpr int kBufBytes = kBlocks * 1024;
 };
 
-// Copy one latent tile (positions [t0, t0+32), rows past `end` replaced by row
-// end-1) into an LDS buffer. Lane i of block k fills LDS chunk 64k + i =
-// (row, pc) and fetches logical chunk pc ^ sw(row) of that row; slack blocks
-// past the tile receive a harmless in-bounds row.
+// Copy one latent tile (32 rows from byte offset `soff` of the buffer
+// `rsrc`) into an LDS buffer. Lane i of block k fills LDS chunk 64k + i =
+// (row, pc) from logical chunk pc ^ sw(row) of that row; voff[k] is that
+// chunk's byte offset within the tile (tile_voffsets). Rows at or past the
+// resource's num_records bytes arrive as zeros.
 //
-// The copy is issued as global_load_lds_dwordx4 in inline assembly: it writes
-// no register, only LDS, and M0 holds the block's LDS address (no other code
-// in these kernels uses M0). Written this way the compiler does not insert a
-// wait for the copy before every later LDS read (it cannot prove that the
-// reads touch another buffer); the kernel waits for the copy itself
+// The copy is issued as buffer_load_dwordx4 ... lds in inline assembly: it
+// writes no register, only LDS, and M0 holds the block's LDS address (no
+// other code in these kernels uses M0). Written this way the compiler does not
+// insert a wait for the copy before every later LDS read (it cannot prove that
+// the reads touch another buffer); the kernel waits for the copy itself
 // (s_waitcnt vmcnt before the barrier that opens the tile).
-// Row r of the tile is read at base + (r - base_row) * 576: for a contiguous
-// cache base is the sequence's first row and base_row = 0; for a paged cache
-// base is the page row that holds t0, base_row = t0 (the tile lies inside one
-// page).
 template <int NWAVES>
-__device__ __forceinline__ void copy_tile(unsigned char* buf, const uint16_t* base, int base_row, int t0,
-                                          int end, int wave, int lane) {
+__device__ __forceinline__ void copy_tile(unsigned char* buf, __amdgpu_buffer_rsrc_t rsrc, uint32_t soff,
+                                          const uint32_t (&voff)[TileCopy<NWAVES>::kPerWave], int wave) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)buf;
 #pragma unroll
   for (int k = 0; k < TileCopy<NWAVES>::kPerWave; ++k) {
-    const int blk = wave + NWAVES * k;
-    const int ci = 64 * blk + lane;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + 1024u * (uint32_t)(wave + NWAVES * k));
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 ::"s"(dst), "v"(voff[k]), "s"(rsrc), "s"(soff) : "memory");
+  }
+}
+
+// Byte offsets within a tile of the chunks this lane copies (see copy_tile);
+// lanes of slack blocks past the tile read row 0 into the slack space.
+template <int NWAVES>
+__device__ __forceinline__ void tile_voffsets(uint32_t (&voff)[TileCopy<NWAVES>::kPerWave], int wave, int lane) {
+#pragma unroll
+  for (int k = 0; k < TileCopy<NWAVES>::kPerWave; ++k) {
+    const int ci = 64 * (wave + NWAVES * k) + lane;
     const int row = ci / kRowChunks, pc = ci % kRowChunks;
-    const bool data = row < kTile;
-    const int lc = data ? pc ^ tile_sw(row) : 0;
-    const int grow = min(t0 + (data ? row : 0), end - 1);
-    const uint16_t* src = base + (size_t)(grow - base_row) * kRow + lc * 8;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + 1024u * (uint32_t)blk);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(dst), "v"(src) : "memory");
+    voff[k] = row < kTile ? (uint32_t)(row * kRow + 8 * (pc ^ tile_sw(row))) * 2u : 0u;
   }
 }
 
@@ -142,16 +145,12 @@ __device__ __forceinline__ void copy_tile(unsigned char* buf, const uint16_t* ba
 // then barrier: afterwards every wave's copies of the current tile are in
 // LDS and every wave is done with the tile before it.
 template <int N>
-__device__ __forceinline__ void wait_tile_barrier(bool next_in_flight) {
-  if (next_in_flight) {
-    if constexpr (N == 36) asm volatile("s_waitcnt vmcnt(36) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else static_assert(N == 9, "no wait defined for this copy count");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  }
+__device__ __forceinline__ void wait_tile_barrier() {
+  if constexpr (N == 36) asm volatile("s_waitcnt vmcnt(36) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else static_assert(N == 9, "no wait defined for this copy count");
 }
 
 // acc *= f on an accumulator tile that lives in AGPRs, in place, through one
@@ -236,6 +235,35 @@ void mla_partial_kernel(const MlaArgs a) {
   const int col = lane & 31;           // this lane's head within the wave's 32
   const int head = hb * (32 * NW) + wave * 32 + col;
 
+  // Latent tiles are read through a buffer resource. Contiguous cache: the
+  // sequence's rows up to its attended length n (rows past n arrive as zeros),
+  // tile t0 at byte offset 1152 t0. Paged cache: the tile's rows inside its
+  // page (pages hold whole tiles: page_size and P are multiples of 32).
+  uint32_t voff[TC::kPerWave];
+  tile_voffsets<NW>(voff, wave, lane);
+  const __amdgpu_buffer_rsrc_t lat_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(lat + (PAGED ? 0 : (size_t)b * T_max * kRow)), 0,
+                                        PAGED ? 0 : n * (kRow * 2), kBufWord3);
+  // Resource and offset for the copy of the tile at t0. Past the partition's
+  // end: a null resource (num_records 0), whose copy only writes zeros into a
+  // free buffer, so that every tile issues the same number of copies.
+  auto tile_src = [&](int t0, __amdgpu_buffer_rsrc_t& r, uint32_t& soff) {
+    if (t0 >= end) {
+      r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(lat), 0, 0, kBufWord3);
+      soff = 0;
+    } else if constexpr (PAGED) {
+      const int phys = min(max(a.block_table[(size_t)b * a.max_pages + (t0 >> a.page_shift)], 0),
+                           a.num_pages - 1);
+      const uint16_t* base = lat + ((size_t)phys * a.page_size + (t0 & (a.page_size - 1))) * kRow;
+      r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, min(kTile, n - t0) * (kRow * 2),
+                                            kBufWord3);
+      soff = 0;
+    } else {
+      r = lat_rsrc;
+      soff = (uint32_t)t0 * (kRow * 2);
+    }
+  };
+
   // Query fragments for all 576 score dims.
   uint4 qf[kSteps];
   {
@@ -252,6 +280,14 @@ void mla_partial_kernel(const MlaArgs a) {
     // in flight, which would stall every tile on its successors' copies.
     __builtin_amdgcn_s_waitcnt(0x0F70);
   }
+  {
+    __amdgpu_buffer_rsrc_t r;
+    uint32_t soff;
+    tile_src(start, r, soff);
+    copy_tile<NW>(bufs[0], r, soff, voff, wave);
+    tile_src(start + kTile, r, soff);
+    copy_tile<NW>(bufs[1], r, soff, voff, wave);
+  }
 
   f32x16 acc[kOTiles];
 #pragma unroll
@@ -260,17 +296,7 @@ void mla_partial_kernel(const MlaArgs a) {
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
   float m = kNegInf, lsum = 0.f;
 
-  const uint16_t* lat_b = lat + (PAGED ? 0 : (size_t)b * T_max * kRow);
-  auto page_base = [&](int t0) -> const uint16_t* {
-    const int phys = min(max(a.block_table[(size_t)b * a.max_pages + (t0 >> a.page_shift)], 0),
-                         a.num_pages - 1);
-    return lat + ((size_t)phys * a.page_size + (t0 & (a.page_size - 1))) * kRow;
-  };
-  auto copy = [&](unsigned char* buf, int t0) {
-    const uint16_t* base = PAGED ? page_base(t0) : lat_b;
-    const int base_row = PAGED ? t0 : 0;
-    copy_tile<NW>(buf, base, base_row, t0, end, wave, lane);
-  };
+
   const int g16 = lane >> 4, i16 = lane & 15;
   const int tr_row = 4 * (g16 >> 1) + (i16 >> 2);
   const int tr_col = 16 * (g16 & 1) + 4 * (i16 & 3);
@@ -289,8 +315,13 @@ void mla_partial_kernel(const MlaArgs a) {
 
   auto tile = [&](const unsigned char* __restrict__ cur_b, unsigned char* __restrict__ nxt_b, int t0) {
     const uint16_t* cur = reinterpret_cast<const uint16_t*>(cur_b);
-    wait_tile_barrier<TC::kPerWave>(t0 + kTile < end);
-    if (t0 + 2 * kTile < end) copy(nxt_b, t0 + 2 * kTile);
+    wait_tile_barrier<TC::kPerWave>();
+    {  // the copy of the tile after next (a null copy past the end)
+      __amdgpu_buffer_rsrc_t r2;
+      uint32_t soff2;
+      tile_src(t0 + 2 * kTile, r2, soff2);
+      copy_tile<NW>(nxt_b, r2, soff2, voff, wave);
+    }
 
     // ---- scores S^T = L . Q^T over all 576 dims
     f32x16 s;
@@ -336,13 +367,18 @@ void mla_partial_kernel(const MlaArgs a) {
     const bool need = mt > m + kTau;
     if (__any(need)) {
       const float f = need ? fast_exp2(m - mt) : 1.f;
+      // Before a head's first weight its accumulators are still zero (m is
+      // -inf); the first tile needs no rescale.
+      const bool scale = __any(need && m != kNegInf);
       m = need ? mt : m;
       lsum *= f;
-      // Matrix-core results are read back only after the wait states the
-      // hardware requires (this path is rare; see scale_acc).
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+      if (scale) {
+        // Matrix-core results are read back only after the wait states the
+        // hardware requires (this path is rare; see scale_acc).
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-      for (int t = 0; t < kOTiles; ++t) scale_acc(acc[t], f);
+        for (int t = 0; t < kOTiles; ++t) scale_acc(acc[t], f);
+      }
     }
     uint32_t ph[8], pl[8];
 #pragma unroll
@@ -391,14 +427,15 @@ void mla_partial_kernel(const MlaArgs a) {
 
   // Tile i sits in buffer i % 3; the copy of tile i + 2 goes into the buffer
   // of tile i - 1, which every wave has finished with at tile i's barrier.
-  copy(bufs[0], start);
-  if (start + kTile < end) copy(bufs[1], start + kTile);
   int cur = 0;
   for (int t0 = start; t0 < end; t0 += kTile) {
     const int nxt = cur == 0 ? 2 : cur - 1;
     tile(bufs[cur], bufs[nxt], t0);
     cur = cur == 2 ? 0 : cur + 1;
   }
+  // The copies issued during the last two tiles (zeros into free buffers)
+  // land before the work-group can end.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // Lanes l and l^32 share a head and a running maximum; add their sums.
   lsum += partner_half(lsum);

@@ -9,8 +9,8 @@
 //
 // One wave per row, four rows per work-group. Lane l owns VW consecutive
 // output elements of each 64*VW-wide slice of the row; the partitions are
-// walked four at a time with independent loads so that several partials of
-// a lane are in flight together. M and the normaliser come from a wave-wide
+// walked eight (then four) at a time with independent loads so that several
+// partials of a lane are in flight together. M and the normaliser come from a wave-wide
 // pass over the log-sum-exps; each partition's weight is then recomputed
 // from its (wave-uniform) log-sum-exp where it is used.
 
@@ -88,6 +88,20 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void lse_merge_kernel(
 #pragma unroll
       for (int i = 0; i < VW; ++i) acc[u][i] = 0.f;
     int p = 0;
+    // Eight partitions at a time: their loads are independent, so a row's
+    // partials arrive in one or two memory round trips, not one per four.
+    for (; p + 8 <= npv; p += 8) {
+      typename V::type x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        x[u] = *reinterpret_cast<const typename V::type*>(po + (size_t)(p + u) * Dv + d0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = fast_exp2(lse[p + u] - M) * invW;
+#pragma unroll
+        for (int i = 0; i < VW; ++i) acc[u & 3][i] = fmaf(w, V::get(x[u], i), acc[u & 3][i]);
+      }
+    }
     for (; p + 4 <= npv; p += 4) {
       typename V::type x[4];
 #pragma unroll

@@ -54,6 +54,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -441,14 +442,33 @@ void mla_partial_kernel(const MlaArgs a) {
   lsum += partner_half(lsum);
   const float inv = 1.f / lsum;
   const size_t prow = ((size_t)b * H + head) * NP + p;
-  float* po = part_out + prow * kDc;
+
+  // The partial output goes out through LDS, one 32-dim slice at a time, so
+  // that every store instruction writes whole 128-byte lines (8 heads x 32
+  // dims) instead of 32-byte pieces of 32 rows. The stores are non-temporal:
+  // the partials are read once, by the merge, and dirty cached copies of them
+  // would otherwise be written back while the next kernel streams its cache.
+  // The staging area is this wave's own blocks of the buffer after the last
+  // tile's: no other wave reads that buffer any more, and this wave's copies
+  // into it have landed.
+  static_assert(TC::kPerWave >= 4, "the staging area is four of this wave's copy blocks");
+  unsigned char* stage = bufs[cur];
+  const int sh = lane >> 3, sc = lane & 7;  // the head (within 8) and 16-byte piece this lane stores
+  const size_t prow0 = ((size_t)b * H + hb * (32 * NW) + wave * 32) * NP + p;
 #pragma unroll
   for (int t = 0; t < kOTiles; ++t) {
 #pragma unroll
-    for (int r = 0; r < 16; r += 4) {
-      const int d = 32 * t + 8 * (r >> 2) + 4 * half;
-      *reinterpret_cast<float4*>(po + d) =
-          make_float4(acc[t][r] * inv, acc[t][r + 1] * inv, acc[t][r + 2] * inv, acc[t][r + 3] * inv);
+    for (int g = 0; g < 4; ++g) {
+      float4* dst = reinterpret_cast<float4*>(stage + 1024 * (wave + NW * (col >> 3)) + 128 * (col & 7) +
+                                              4 * (8 * g + 4 * half));
+      *dst = make_float4(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv, acc[t][4 * g + 2] * inv,
+                         acc[t][4 * g + 3] * inv);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stage + 1024 * (wave + NW * k) + 16 * lane);
+      float* po = part_out + (prow0 + (size_t)(8 * k + sh) * NP) * kDc + 32 * t + 4 * sc;
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(po));
     }
   }
   if (half == 0) part_lse[prow] = m + fast_log2(lsum);

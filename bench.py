@@ -369,18 +369,30 @@ def main():
         if kind == "gqa":
             q, k, v, gl = gpu
             P, NP, ws = m.attn_decode_gqa_plan(w.B, w.h_q, w.h_kv, w.D, w.T_max, w.dtype)
-            po = torch.empty((w.B, w.h_q, NP, w.D), dtype=torch.float32, device=dev)
-            pl = torch.empty((w.B, w.h_q, NP), dtype=torch.float32, device=dev)
             out = torch.empty_like(q)
             kv, other, flops = gqa_work(w, lens)
+            if w.dtype == torch.bfloat16 and w.group <= 8:
+                # attn_decode_gqa's work-balanced split, one stage per call
+                wsb = torch.empty(ws, dtype=torch.uint8, device=dev)
+                P, NP = "work-balanced split, 128-position units", None
 
-            def partial(q=q, k=k, v=v, gl=gl, P=P, po=po, pl=pl, w=w):
-                m.attn_decode_gqa_partial(q, k, v, gl, P, scale=w.scale, part_out=po, part_lse=pl)
+                def partial(q=q, k=k, v=v, gl=gl, wsb=wsb, out=out, w=w):
+                    m.attn_decode_gqa_split(q, k, v, gl, wsb, scale=w.scale, out=out)
 
-            def merge(po=po, pl=pl, gl=gl, P=P, out=out, w=w):
-                m.attn_decode_merge(po, pl, gl, w.T_max, P, out=out)
-            kname = (f"gqa_partial_po_kernel<{w.D}, {w.group}>" if w.group <= 8
-                     else f"gqa_partial_kernel<BF16Elem, {w.D}, {w.group}>")
+                def merge(q=q, k=k, v=v, gl=gl, wsb=wsb, out=out, w=w):
+                    m.attn_decode_gqa_split_merge(q, k, v, gl, wsb, scale=w.scale, out=out)
+                kname = f"gqa_partial_po_kernel<{w.D}, {w.group}, true>"
+            else:
+                po = torch.empty((w.B, w.h_q, NP, w.D), dtype=torch.float32, device=dev)
+                pl = torch.empty((w.B, w.h_q, NP), dtype=torch.float32, device=dev)
+
+                def partial(q=q, k=k, v=v, gl=gl, P=P, po=po, pl=pl, w=w):
+                    m.attn_decode_gqa_partial(q, k, v, gl, P, scale=w.scale, part_out=po, part_lse=pl)
+
+                def merge(po=po, pl=pl, gl=gl, P=P, out=out, w=w):
+                    m.attn_decode_merge(po, pl, gl, w.T_max, P, out=out)
+                kname = (f"gqa_partial_po_kernel<{w.D}, {w.group}, false>" if w.group <= 8
+                         else f"gqa_partial_kernel<BF16Elem, {w.D}, {w.group}>")
             src = os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "gqa_decode.hip")
         else:
             qn, qr, lat, gl = gpu

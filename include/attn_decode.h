@@ -51,6 +51,14 @@
  *   points expose the two stages (for a caller that merges partials itself,
  *   e.g. across devices); the one-call entry points run both with the
  *   library's own partition size and a caller-provided workspace.
+ * - bf16 GQA with D in {64, 128} and g in {1, 2, 4, 8} (contiguous caches, and
+ *   paged caches whose pages are a multiple of 32 positions) is split
+ *   differently by the one-call entry points: every resident work-group takes
+ *   an equal share of all (sequence, KV head, 128-position unit) work, and
+ *   each work-group's share of a (sequence, KV head) row is one partial. The
+ *   cut points then depend on the sequence lengths and on the device's
+ *   compute-unit count; on one device the output is still bit-identical
+ *   from run to run.
  */
 #ifndef ATTN_DECODE_H
 #define ATTN_DECODE_H
@@ -108,9 +116,11 @@ uint64_t attn_mla_cache_bytes(uint64_t n_layers, uint64_t d_c, uint64_t d_r,
  * (ATTN_ERR_UNSUPPORTED otherwise).
  */
 
-/* The library's plan for a shape: partition size (positions per split),
- * number of partitions ceil(T_max / partition_size), and the workspace bytes
- * attn_decode_gqa needs. Outputs may be NULL. Returns a status. */
+/* The library's plan for a shape: partition size (positions per split, as
+ * attn_decode_gqa_partial would use it), number of partitions
+ * ceil(T_max / partition_size), and the workspace bytes attn_decode_gqa needs
+ * on the current device (the work-balanced split's partials scale with its
+ * compute-unit count). Outputs may be NULL. Returns a status. */
 int attn_decode_gqa_plan(int B, int h_q, int h_kv, int D, int T_max, attn_dtype dt,
                          int* partition_size, int* num_partitions, size_t* workspace_bytes);
 
@@ -125,6 +135,25 @@ int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* seq_lens, int B, int h_q, int h_kv, int D, int T_max,
                     float scale, attn_dtype dt, void* out,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The two stages of attn_decode_gqa where it runs the work-balanced split
+ * (bf16, D in {64, 128}, g in {1, 2, 4, 8}; ATTN_ERR_UNSUPPORTED for other
+ * shapes). They take exactly attn_decode_gqa's arguments and checks.
+ * attn_decode_gqa_split runs stage 1 only: it writes the partials into the
+ * workspace and does not touch `out`. attn_decode_gqa_split_merge runs stage 2
+ * only: it reads those partials and seq_lens (which must not have changed)
+ * and writes `out`; q, k_cache and v_cache are checked but not read. Both
+ * must run on the same device, in stream order, with the same shape and
+ * workspace; together they produce the same bits as attn_decode_gqa. They
+ * exist so that each stage can be timed on its own. */
+int attn_decode_gqa_split(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* seq_lens, int B, int h_q, int h_kv, int D, int T_max,
+                          float scale, attn_dtype dt, void* out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+int attn_decode_gqa_split_merge(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* seq_lens, int B, int h_q, int h_kv, int D, int T_max,
+                                float scale, attn_dtype dt, void* out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Sliding-window decode ("Grouped-Query Attention: Fewer KV Heads, Same
  * Quality", section "GQA and Related KV-Head Choices in Modern Architectures":

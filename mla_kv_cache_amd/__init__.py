@@ -23,6 +23,7 @@ __all__ = [
     "AttnError", "load",
     "attn_kv_cache_bytes", "attn_mla_cache_bytes",
     "attn_decode_gqa_plan", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa",
+    "attn_decode_gqa_split", "attn_decode_gqa_split_merge",
     "attn_decode_gqa_partial", "attn_decode_merge",
     "attn_decode_mla_plan", "attn_decode_mla_workspace_bytes", "attn_decode_mla",
     "attn_decode_mla_partial",
@@ -150,6 +151,38 @@ def attn_decode_gqa(q, k_cache, v_cache, seq_lens, scale: Optional[float] = None
                                   workspace.numel() * workspace.element_size(), _stream(dev)),
            "attn_decode_gqa")
     return out
+
+
+def _gqa_split_call(fn_name, q, k_cache, v_cache, seq_lens, workspace, scale, out):
+    B, h_q, h_kv, D, T_max = _gqa_shapes(q, k_cache, v_cache)
+    dev = _dev(q, k_cache, v_cache, seq_lens)
+    _lens(seq_lens, B)
+    dt = _dt(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, workspace)
+    _check(getattr(load(), fn_name)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B, h_q,
+                                    h_kv, D, T_max, scale, dt, _ptr(out), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(dev)),
+           fn_name)
+    return out
+
+
+def attn_decode_gqa_split(q, k_cache, v_cache, seq_lens, workspace: torch.Tensor,
+                          scale: Optional[float] = None, out: Optional[torch.Tensor] = None):
+    """Stage 1 of attn_decode_gqa's work-balanced split (bf16, D in {64,128}, g in {1,2,4,8}):
+    writes the partials into `workspace` (attn_decode_gqa_workspace_bytes bytes); `out` is
+    checked, not written."""
+    _gqa_split_call("attn_decode_gqa_split", q, k_cache, v_cache, seq_lens, workspace, scale, out)
+
+
+def attn_decode_gqa_split_merge(q, k_cache, v_cache, seq_lens, workspace: torch.Tensor,
+                                scale: Optional[float] = None, out: Optional[torch.Tensor] = None):
+    """Stage 2 of the split: merges the partials stage 1 left in `workspace` into
+    out [B, h_q, D] (returned)."""
+    return _gqa_split_call("attn_decode_gqa_split_merge", q, k_cache, v_cache, seq_lens, workspace,
+                           scale, out)
 
 
 def attn_decode_gqa_window(q, k_cache, v_cache, seq_lens, window: int, scale: Optional[float] = None,

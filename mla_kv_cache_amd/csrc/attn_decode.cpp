@@ -5,6 +5,8 @@
 #include "attn_decode.h"
 
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 #include <string.h>
 
@@ -78,6 +80,16 @@ int gqa_auto_partition(const GqaShape& s) {
 
 size_t partial_bytes(int64_t rows, int NP, int Dv) {
   return align_up(size_t(rows) * NP * Dv * sizeof(float)) + align_up(size_t(rows) * NP * sizeof(float));
+}
+
+// Split decode: work-groups of the launch (0: the shape does not take it) and
+// its workspace, one partial per slot (work-groups + B * h_kv slots of G heads).
+int gqa_split_groups(const GqaShape& s) {
+  const int G = s.h_q / s.h_kv;
+  return attn::gqa_persistent(int(s.dt), s.D, G) ? attn::gqa_split_groups(s.D, G) : 0;
+}
+size_t split_bytes(const GqaShape& s, int groups) {
+  return partial_bytes((int64_t(groups) + int64_t(s.B) * s.h_kv) * (s.h_q / s.h_kv), 1, s.D);
 }
 
 // ------------------------------------------------------------------ MLA plan
@@ -219,8 +231,10 @@ int attn_decode_gqa_plan(int B, int h_q, int h_kv, int D, int T_max, attn_dtype 
   if (st != ATTN_OK) return st;
   const int P = gqa_auto_partition(s);
   const int NP = ceil_div(T_max, P);
-  return set_plan(P, T_max, partial_bytes(int64_t(B) * h_q, NP, D), partition_size,
-                  num_partitions, workspace_bytes);
+  const int groups = gqa_split_groups(s);
+  size_t ws = partial_bytes(int64_t(B) * h_q, NP, D);
+  if (groups > 0) ws = std::max(ws, split_bytes(s, groups));
+  return set_plan(P, T_max, ws, partition_size, num_partitions, workspace_bytes);
 }
 
 size_t attn_decode_gqa_workspace_bytes(int B, int h_q, int h_kv, int D, int T_max, attn_dtype dt) {
@@ -293,7 +307,8 @@ namespace {
 int gqa_decode_impl(const void* q, const void* k_new, const void* v_new, const void* k_cache,
                     const void* v_cache, const int32_t* seq_lens, int B, int h_q, int h_kv, int D,
                     int T_max, int window, float scale, attn_dtype dt, void* out, void* workspace,
-                    size_t workspace_bytes, hipStream_t stream, const Paged& pg = Paged()) {
+                    size_t workspace_bytes, hipStream_t stream, const Paged& pg = Paged(),
+                    int stages = 3) {
   const GqaShape s{B, h_q, h_kv, D, T_max, dt};
   int st = check_gqa_shape(s);
   if (st != ATTN_OK) return st;
@@ -319,12 +334,15 @@ int gqa_decode_impl(const void* q, const void* k_new, const void* v_new, const v
     st = check_gqa_ptrs(s, q, k_cache, v_cache, seq_lens, out, out_b);
     if (st != ATTN_OK) return st;
   }
+  // The split decode serves the persistent kernel's shapes (and paged caches
+  // whose pages hold whole 32-row tiles); the others run on fixed partitions.
   // A window attends over at most `window` positions: plan for that span.
+  const int groups = (!pg.block_table || pg.page_size % 32 == 0) ? gqa_split_groups(s) : 0;
   const int span = window > 0 && window < T_max ? window : T_max;
   const GqaShape sp{B, h_q, h_kv, D, span, dt};
-  const int P = gqa_auto_partition(sp);
-  const int NP = ceil_div(span, P);
-  const size_t need = partial_bytes(int64_t(B) * h_q, NP, D);
+  const int P = groups > 0 ? attn::kSplitUnit : gqa_auto_partition(sp);
+  const int NP = groups > 0 ? 0 : ceil_div(span, P);
+  const size_t need = groups > 0 ? split_bytes(s, groups) : partial_bytes(int64_t(B) * h_q, NP, D);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
   const size_t kb = pg.block_table ? size_t(pg.num_pages) * h_kv * pg.page_size * D * elem_size(dt)
@@ -337,12 +355,21 @@ int gqa_decode_impl(const void* q, const void* k_new, const void* v_new, const v
     st = check_new_rows(s, k_new, v_new, q, k_cache, v_cache, seq_lens, out, out_b, workspace, need);
     if (st != ATTN_OK) return st;
   }
+  const size_t rows = groups > 0 ? (size_t(groups) + size_t(B) * h_kv) * (h_q / h_kv) : size_t(B) * h_q * NP;
   float* part_out = static_cast<float*>(workspace);
-  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                             align_up(size_t(B) * h_q * NP * D * sizeof(float)));
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(rows * D * sizeof(float)));
   const attn::GqaArgs a{q, k_cache, v_cache, seq_lens, k_new, v_new, window, pg.block_table,
                         pg.page_size, pg.page_shift, pg.max_pages, pg.num_pages, B, h_kv, T_max,
                         P, NP, float(double(scale) * kLog2e), part_out, part_lse};
+  if (groups > 0) {
+    if ((stages & 1) && attn::launch_gqa_split(D, h_q / h_kv, a, groups, stream) != hipSuccess)
+      return ATTN_ERR_HIP;
+    if ((stages & 2) && attn::launch_split_merge(int(dt), part_out, part_lse, seq_lens, k_new ? 1 : 0, window,
+                                                 B, h_kv, h_q / h_kv, D, T_max, groups, out, stream) != hipSuccess)
+      return ATTN_ERR_HIP;
+    return ATTN_OK;
+  }
+  if (stages != 3) return ATTN_ERR_UNSUPPORTED;
   if (attn::launch_gqa_partial(int(dt), D, h_q / h_kv, a, stream) != hipSuccess) return ATTN_ERR_HIP;
   if (attn::launch_merge(int(dt), part_out, part_lse, seq_lens, k_new ? 1 : 0, window, B, h_q, D,
                          T_max, P, NP, out, stream) != hipSuccess)
@@ -360,6 +387,22 @@ int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
                     size_t workspace_bytes, hipStream_t stream) {
   return gqa_decode_impl(q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, h_q, h_kv, D, T_max,
                          0, scale, dt, out, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_gqa_split(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* seq_lens, int B, int h_q, int h_kv, int D, int T_max,
+                          float scale, attn_dtype dt, void* out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  return gqa_decode_impl(q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, h_q, h_kv, D, T_max,
+                         0, scale, dt, out, workspace, workspace_bytes, stream, Paged(), 1);
+}
+
+int attn_decode_gqa_split_merge(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* seq_lens, int B, int h_q, int h_kv, int D, int T_max,
+                                float scale, attn_dtype dt, void* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  return gqa_decode_impl(q, nullptr, nullptr, k_cache, v_cache, seq_lens, B, h_q, h_kv, D, T_max,
+                         0, scale, dt, out, workspace, workspace_bytes, stream, Paged(), 2);
 }
 
 int attn_decode_gqa_window(const void* q, const void* k_cache, const void* v_cache,

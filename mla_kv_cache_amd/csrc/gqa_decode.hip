@@ -633,6 +633,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // every work-group gets the same number of partitions (give or take one)
 // whatever the mix of sequence lengths, and consecutive items mostly share
 // one query and one KV head.
+//
+// Split mode: the items are units of kSplitUnit positions (one 32-row tile
+// per wave), and a work-group treats the consecutive units of its run that
+// belong to one (b, j) as one segment, with one partial output. Every
+// work-group then streams the same number of units (give or take one), and
+// a (b, j) row is split between work-groups only where a run boundary falls.
+// The partial of work-group w's segment of pair (b, j) goes to slot
+// w + b * h_kv + j: along a run both w and the pair index only grow, so the
+// slots are distinct, and the segments of one pair sit in consecutive slots
+// (those of the work-groups whose run meets its units).
 struct ItemRun {
   long long left;  // items still to do, the current one included
   int b, j, p;     // current item
@@ -714,7 +724,7 @@ __device__ __forceinline__ void next_item(ItemRun& r, const GqaArgs& a) {
   } while (r.b < a.B && (r.np = partitions_of(a, r.b)) == 0);
 }
 
-template <int D, int G>
+template <int D, int G, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs a) {
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
   // Not restrict: a decode step writes one row of each cache before reading.
@@ -819,10 +829,13 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
 
   for (ItemRun run = first_item(a); run.left > 0 && run.b < a.B;) {
     const int b = run.b, j = run.j, p = run.p;
+    // Units (or partitions) of (b, j) this item covers: split mode takes all
+    // of the run's remaining units of the pair at once.
+    const int len = SPLIT ? (int)min((long long)(run.np - run.p), run.left) : 1;
     const int len0 = a.seq_lens[b];
     const int n = attended_len(len0, a.k_new ? 1 : 0, T_max);
     const int start = window_lo(n, a.window) + p * P;
-    const int end = min(start, n - P) + P;
+    const int end = min(n - start, len * P) + start;
     if (a.k_new) {  // decode step: the work-group that reads the new row writes it first
       const int pos = max(len0, 0);
       if (pos < T_max && pos >= start && pos < end) {
@@ -974,15 +987,17 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
     // the copy overlaps the combine below (not in a decode step, whose next
     // item may first have to write its new row).
     ItemRun nrun = run;
-    bool have_next = run.left > 1;
+    bool have_next = run.left > len;
     if (have_next) {
+      nrun.p = run.p + len - 1;
       next_item(nrun, a);
       have_next = nrun.b < a.B;
     }
     if (have_next && !a.k_new) {
+      const int nlen = SPLIT ? (int)min((long long)(nrun.np - nrun.p), run.left - len) : 1;
       const int nn = attended_len(a.seq_lens[nrun.b], 0, T_max);
       const int nstart = window_lo(nn, a.window) + nrun.p * P;
-      const int nend = min(nstart, nn - P) + P;
+      const int nend = min(nn - nstart, nlen * P) + nstart;
       if (nstart + wave * TR < nend) {
         __amdgpu_buffer_rsrc_t krt, vrt;
         uint32_t toff;
@@ -1033,13 +1048,14 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
         Ls += sm_l[par][w2][h] * f;
         A += comb[par][w2][h][d] * f;
       }
-      const size_t row = ((size_t)b * H + (size_t)j * G + h) * NP + p;
+      const size_t row = SPLIT ? (size_t)(blockIdx.x + (long long)b * h_kv + j) * G + h
+                               : ((size_t)b * H + (size_t)j * G + h) * NP + p;
       part_out[row * D + d] = A / Ls;
       if (d == 0) part_lse[row] = M + fast_log2(Ls);
     }
     par ^= 1;
     if (!have_next) break;
-    nrun.left = run.left - 1;
+    nrun.left = run.left - len;
     run = nrun;
   }
 }
@@ -1056,26 +1072,45 @@ int device_cus() {
   return n;
 }
 
+// Work-groups of the persistent kernel one CU holds at once.
+template <int D, int G, bool SPLIT>
+int po_per_cu() {
+  static const int per_cu = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &nb, reinterpret_cast<const void*>(&gqa_partial_po_kernel<D, G, SPLIT>), kThreads, 0) != hipSuccess ||
+        nb < 1)
+      nb = 1;
+    return nb;
+  }();
+  return per_cu;
+}
+
 // The persistent kernel is launched with as many work-groups as the device
 // holds at once (never more than there are partitions); each takes an equal
 // share of the non-empty partitions.
 template <int D, int G>
 hipError_t launch_po(const GqaArgs& a, hipStream_t stream) {
-  constexpr auto kernel = &gqa_partial_po_kernel<D, G>;
-  static const int per_cu = [] {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(kernel), kThreads, 0) !=
-            hipSuccess ||
-        nb < 1)
-      nb = 1;
-    return nb;
-  }();
   const int cus = device_cus();
   if (cus <= 0) return hipErrorInvalidDevice;
   const long long items = (long long)a.B * a.h_kv * a.NP;
-  const int grid = (int)std::min<long long>(items, (long long)cus * per_cu);
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  const int grid = (int)std::min<long long>(items, (long long)cus * po_per_cu<D, G, false>());
+  hipLaunchKernelGGL((gqa_partial_po_kernel<D, G, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+static_assert(kSplitUnit == kWaves * kPoRows, "a split unit is one tile per wave");
+
+// Work-groups per CU of the split launch (at most what the CU holds). At
+// g = 8 a wave's arithmetic per byte needs two waves per SIMD to keep up with
+// the memory stream (one work-group per CU: 248 us for the 70B-shaped layer,
+// two: 186 us); at g <= 4 one work-group per CU, with the longest runs and the
+// fewest combines, is fastest (8B-shaped layer: 95 us against 98 with two).
+template <int D, int G>
+int split_groups_dg() {
+  const int cus = device_cus();
+  if (cus <= 0) return 0;
+  return cus * std::min(G >= 8 ? 2 : 1, po_per_cu<D, G, true>());
 }
 
 template <class E, int D, int G>
@@ -1138,6 +1173,37 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const unsigned char* __r
 }
 
 }  // namespace
+
+int gqa_split_groups(int D, int group) {
+  switch (D * 16 + group) {
+    case 128 * 16 + 1: return split_groups_dg<128, 1>();
+    case 128 * 16 + 2: return split_groups_dg<128, 2>();
+    case 128 * 16 + 4: return split_groups_dg<128, 4>();
+    case 128 * 16 + 8: return split_groups_dg<128, 8>();
+    case 64 * 16 + 1: return split_groups_dg<64, 1>();
+    case 64 * 16 + 2: return split_groups_dg<64, 2>();
+    case 64 * 16 + 4: return split_groups_dg<64, 4>();
+    case 64 * 16 + 8: return split_groups_dg<64, 8>();
+    default: return 0;
+  }
+}
+
+hipError_t launch_gqa_split(int D, int group, const GqaArgs& a, int groups, hipStream_t s) {
+  if (groups < 1) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)groups), block(kThreads);
+  switch (D * 16 + group) {
+    case 128 * 16 + 1: hipLaunchKernelGGL((gqa_partial_po_kernel<128, 1, true>), grid, block, 0, s, a); break;
+    case 128 * 16 + 2: hipLaunchKernelGGL((gqa_partial_po_kernel<128, 2, true>), grid, block, 0, s, a); break;
+    case 128 * 16 + 4: hipLaunchKernelGGL((gqa_partial_po_kernel<128, 4, true>), grid, block, 0, s, a); break;
+    case 128 * 16 + 8: hipLaunchKernelGGL((gqa_partial_po_kernel<128, 8, true>), grid, block, 0, s, a); break;
+    case 64 * 16 + 1: hipLaunchKernelGGL((gqa_partial_po_kernel<64, 1, true>), grid, block, 0, s, a); break;
+    case 64 * 16 + 2: hipLaunchKernelGGL((gqa_partial_po_kernel<64, 2, true>), grid, block, 0, s, a); break;
+    case 64 * 16 + 4: hipLaunchKernelGGL((gqa_partial_po_kernel<64, 4, true>), grid, block, 0, s, a); break;
+    case 64 * 16 + 8: hipLaunchKernelGGL((gqa_partial_po_kernel<64, 8, true>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 bool gqa_persistent(int dt, int D, int group) {
   return dt == 1 && (D == 64 || D == 128) && group >= kPoMinGroup && group <= 8 && (group & (group - 1)) == 0;

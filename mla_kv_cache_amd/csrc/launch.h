@@ -35,6 +35,20 @@ struct GqaArgs {
 
 hipError_t launch_gqa_partial(int dt, int D, int group, const GqaArgs& a, hipStream_t stream);
 
+// Split decode: the persistent kernel in split mode (bf16, gqa_persistent
+// shapes). The work is cut into units of kSplitUnit positions of one
+// (sequence, KV head) pair; `groups` work-groups each take an equal
+// contiguous run of the units, and the run's part of each pair becomes one
+// partial in slot (work-group + b * h_kv + j): part_out [groups + B*h_kv, G, D],
+// part_lse [groups + B*h_kv, G]. a.P must be kSplitUnit; a.NP is not used.
+constexpr int kSplitUnit = 128;
+int gqa_split_groups(int D, int group);  // work-groups of the split launch on the current device
+hipError_t launch_gqa_split(int D, int group, const GqaArgs& a, int groups, hipStream_t stream);
+// Merge of the split partials into out [B, h_kv * group, D].
+hipError_t launch_split_merge(int out_dt, const float* part_out, const float* part_lse,
+                              const int32_t* seq_lens, int len_add, int window, int B, int h_kv,
+                              int group, int D, int T_max, int groups, void* out, hipStream_t stream);
+
 // Plain copy of the new K/V rows into the caches (the decode step's write alone).
 hipError_t launch_kv_append(int dt, const void* k_new, const void* v_new, void* k, void* v,
                             const int32_t* seq_lens, int B, int h_kv, int D, int T_max,

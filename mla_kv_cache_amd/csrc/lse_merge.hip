@@ -146,7 +146,140 @@ hipError_t launch_typed(const float* part_out, const float* part_lse, const int3
   return hipGetLastError();
 }
 
+__device__ __forceinline__ long long wave_sum_i64(long long x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Units (of kSplitUnit positions) of sequence b in a split decode.
+__device__ __forceinline__ long long split_units(const int32_t* seq_lens, int b, int len_add, int window,
+                                                 int T_max) {
+  const int n = attended_len(seq_lens[b], len_add, T_max);
+  return (n - window_lo(n, window) + kSplitUnit - 1) / kSplitUnit;
+}
+
+// Merge of the split partials (stage 2 of a split decode). Row (b, h) belongs
+// to pair pi = b * h_kv + h / G, whose units are [base, base + units) of the
+// U units of the launch (pairs in order, b-major). Work-group w of the NW
+// split work-groups held units [U w / NW, U (w + 1) / NW) and wrote the
+// partial of its share of each pair to slot w + pi, so the pair's partials
+// are the slots of the work-groups from the one holding unit base to the one
+// holding unit base + units - 1, leaving out work-groups whose run was empty
+// (only when U < NW). The merge itself is the same log-sum-exp regrouping as
+// for fixed partitions. One wave per row, four rows per work-group.
+template <typename TO, int VW>
+__global__ __launch_bounds__(64 * kRowsPerGroup) void split_merge_kernel(
+    const float* __restrict__ part_out, const float* __restrict__ part_lse,
+    const int32_t* __restrict__ seq_lens, int len_add, int window, int B, int h_kv, int G, int Dv,
+    int T_max, int NW, TO* __restrict__ out) {
+  using V = Vec<VW>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = h_kv * G;
+  const int row = blockIdx.x * kRowsPerGroup + wave;  // b * H + h, uniform in the wave
+  if (row >= B * H) return;
+  const int b = row / H, h = row % H, j = h / G, hh = h % G;
+  TO* o = out + (size_t)row * Dv;
+
+  long long before = 0, total = 0;  // units of the sequences before b, of all sequences
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int bb = b0 + lane;
+    const long long u = bb < B ? split_units(seq_lens, bb, len_add, window, T_max) : 0;
+    total += wave_sum_i64(u);
+    before += wave_sum_i64(bb < b ? u : 0);
+  }
+  const long long units = split_units(seq_lens, b, len_add, window, T_max);
+  if (units == 0) {  // nothing attended: the row is zeros
+    float z[VW];
+#pragma unroll
+    for (int i = 0; i < VW; ++i) z[i] = 0.f;
+    for (int d0 = lane * VW; d0 < Dv; d0 += 64 * VW) store_out<VW>(o + d0, z);
+    return;
+  }
+  const long long U = total * h_kv;
+  const long long base = before * h_kv + (long long)j * units;
+  // Work-group holding unit u: the largest w with U w / NW <= u.
+  auto holder = [&](long long u) { return (int)(((u + 1) * NW - 1) / U); };
+  auto held = [&](int w) { return U * (w + 1) / NW > U * w / NW; };
+  const int w0 = holder(base), w1 = holder(base + units - 1);
+  const long long pi = (long long)b * h_kv + j;
+  const int ns = w1 - w0 + 1;
+  auto slot_row = [&](int s) { return ((size_t)(w0 + s + pi) * G + hh); };
+
+  float M = kNegInf;
+  for (int s = lane; s < ns; s += 64)
+    if (held(w0 + s)) M = fmaxf(M, part_lse[slot_row(s)]);
+  M = wave_max(M);
+  float W = 0.f;
+  for (int s = lane; s < ns; s += 64)
+    if (held(w0 + s)) W += fast_exp2(part_lse[slot_row(s)] - M);
+  const float invW = 1.f / wave_sum(W);
+
+  for (int d0 = lane * VW; d0 < Dv; d0 += 64 * VW) {
+    float acc[4][VW];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < VW; ++i) acc[u][i] = 0.f;
+    int s = 0;
+    if (U >= NW) {  // every run holds at least one unit: all slots in [w0, w1] are written
+      for (; s + 4 <= ns; s += 4) {
+        typename V::type x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          x[u] = *reinterpret_cast<const typename V::type*>(part_out + slot_row(s + u) * Dv + d0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float w = fast_exp2(part_lse[slot_row(s + u)] - M) * invW;
+#pragma unroll
+          for (int i = 0; i < VW; ++i) acc[u][i] = fmaf(w, V::get(x[u], i), acc[u][i]);
+        }
+      }
+    }
+    for (; s < ns; ++s) {
+      if (!held(w0 + s)) continue;
+      const typename V::type x = *reinterpret_cast<const typename V::type*>(part_out + slot_row(s) * Dv + d0);
+      const float w = fast_exp2(part_lse[slot_row(s)] - M) * invW;
+#pragma unroll
+      for (int i = 0; i < VW; ++i) acc[0][i] = fmaf(w, V::get(x, i), acc[0][i]);
+    }
+    float r[VW];
+#pragma unroll
+    for (int i = 0; i < VW; ++i) r[i] = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+    store_out<VW>(o + d0, r);
+  }
+}
+
+template <typename TO>
+hipError_t launch_split_typed(const float* part_out, const float* part_lse, const int32_t* seq_lens,
+                              int len_add, int window, int B, int h_kv, int G, int Dv, int T_max,
+                              int NW, TO* out, hipStream_t stream) {
+  const long long rows = (long long)B * h_kv * G;
+  if ((rows + kRowsPerGroup - 1) / kRowsPerGroup > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)((rows + kRowsPerGroup - 1) / kRowsPerGroup));
+  const dim3 block(64 * kRowsPerGroup);
+  if (Dv % 128 == 0)
+    hipLaunchKernelGGL((split_merge_kernel<TO, 2>), grid, block, 0, stream, part_out, part_lse, seq_lens,
+                       len_add, window, B, h_kv, G, Dv, T_max, NW, out);
+  else
+    hipLaunchKernelGGL((split_merge_kernel<TO, 1>), grid, block, 0, stream, part_out, part_lse, seq_lens,
+                       len_add, window, B, h_kv, G, Dv, T_max, NW, out);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_split_merge(int out_dt, const float* part_out, const float* part_lse,
+                              const int32_t* seq_lens, int len_add, int window, int B, int h_kv,
+                              int group, int D, int T_max, int groups, void* out, hipStream_t stream) {
+  if (groups < 1) return hipErrorInvalidValue;
+  if (out_dt == 0)
+    return launch_split_typed(part_out, part_lse, seq_lens, len_add, window, B, h_kv, group, D, T_max,
+                              groups, static_cast<float*>(out), stream);
+  return launch_split_typed(part_out, part_lse, seq_lens, len_add, window, B, h_kv, group, D, T_max,
+                            groups, static_cast<uint16_t*>(out), stream);
+}
 
 bool merge_supported(int out_dt, int Dv) {
   return (out_dt == 0 || out_dt == 1) && Dv >= 4 && Dv % 4 == 0 && Dv <= 1024;

@@ -238,3 +238,48 @@ def test_persistent_split_many_sequences(gpu, B, h_q, h_kv, D):
         assert float(np.abs(got - ref).max()) <= 2e-3, P
     empty = (lens == 0).nonzero().flatten().tolist()
     assert torch.equal(out[empty], torch.zeros_like(out[empty]))
+
+
+@pytest.mark.parametrize("B,h_q,h_kv,D,T,seed", [
+    (3, 32, 8, 128, 1000, 31),     # a few pairs over many work-groups
+    (1, 8, 8, 64, 40, 32),         # fewer units than work-groups: runs left empty
+    (40, 64, 8, 128, 2000, 33),    # ragged, pairs cut between work-groups
+    (2, 8, 1, 128, 700, 34),       # MQA
+    (5, 16, 8, 64, 130, 35),       # units of one and two tiles' worth
+])
+def test_split_stages_match_one_call(gpu, B, h_q, h_kv, D, T, seed):
+    """The work-balanced split: its two stages called one after the other give
+    the bits of the one-call entry point, which matches the oracle, for shapes
+    where the units are fewer than the work-groups (empty runs are skipped by
+    the merge) and where rows are cut between work-groups."""
+    m = _m()
+    g = torch.Generator().manual_seed(seed)
+    lens = torch.randint(0, T + 1, (B,), generator=g, dtype=torch.int32)
+    lens[0] = T
+    if B > 2:
+        lens[1] = 0
+    w = W.small_gqa(B, h_q, h_kv, D, T, seed=seed)
+    (q, k, v, l), (gq, gk, gv, gl) = _inputs(w, gpu, lens)
+    ws = torch.empty(m.attn_decode_gqa_workspace_bytes(B, h_q, h_kv, D, T), dtype=torch.uint8, device=gpu)
+    full = m.attn_decode_gqa(gq, gk, gv, gl, scale=w.scale)
+    m.attn_decode_gqa_split(gq, gk, gv, gl, ws, scale=w.scale)
+    got = m.attn_decode_gqa_split_merge(gq, gk, gv, gl, ws, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(got, full)
+    ref = oracle.decode_gqa(q, k, v, l, w.scale)
+    assert np.all(np.abs(_f64(full) - ref) <= 2e-3 + _half_ulp_bf16(ref))
+    zero = (lens == 0).nonzero().flatten().tolist()
+    assert torch.equal(full[zero], torch.zeros_like(full[zero]))
+
+
+def test_split_stages_reject_unsplit_shapes(gpu):
+    """fp32 and g = 16 run on fixed partitions: the stage entry points say so."""
+    m = _m()
+    for dt, h_q, h_kv in ((torch.float32, 8, 2), (torch.bfloat16, 16, 1)):
+        w = W.small_gqa(2, h_q, h_kv, 128, 64, dtype=dt, seed=36)
+        _, (gq, gk, gv, gl) = _inputs(w, gpu)
+        ws = torch.empty(1 << 20, dtype=torch.uint8, device=gpu)
+        with pytest.raises(m.AttnError):
+            m.attn_decode_gqa_split(gq, gk, gv, gl, ws)
+        with pytest.raises(m.AttnError):
+            m.attn_decode_gqa_split_merge(gq, gk, gv, gl, ws)

@@ -948,11 +948,15 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
         }
       }
       // Both halves hold every score; the lanes of half 0 own the weights.
+      // A position past the end has score -inf and weight exp2(-inf) = 0 (m
+      // is finite: every tile starts at a valid position). Both halves add
+      // the same weights to lpart; the final sum is halved (exactly: the two
+      // halves reduce identical values in the same order).
       float w[GP];
 #pragma unroll
       for (int h = 0; h < GP; ++h) {
-        w[h] = (h < G && valid) ? fast_exp2(s[h < G ? h : 0] - m[h < G ? h : 0]) : 0.f;
-        if (h < G) lpart[h] += hf ? 0.f : w[h];
+        w[h] = h < G ? fast_exp2(s[h < G ? h : 0] - m[h < G ? h : 0]) : 0.f;
+        if (h < G) lpart[h] += w[h];
       }
       if (hf == 0) {
 #pragma unroll
@@ -1012,7 +1016,7 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
     float L[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      L[h] = wave_sum(lpart[h]);
+      L[h] = 0.5f * wave_sum(lpart[h]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float x = acc[h][e];

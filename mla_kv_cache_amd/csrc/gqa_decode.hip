@@ -391,8 +391,10 @@ __device__ __forceinline__ void dot_chunk8(float (&acc)[8], const uint32_t (&qr)
       : "v"(qr[0]), "v"(qr[1]), "v"(qr[2]), "v"(qr[3]), "v"(qr[4]), "v"(qr[5]), "v"(qr[6]), "v"(qr[7]), "v"(k.x), "v"(k.y), "v"(k.z), "v"(k.w), "i"(L0 + 0), "i"(L0 + 1), "i"(L0 + 2), "i"(L0 + 3));
 }
 
-// Maximum over all 64 lanes of N values per lane (four DPP steps inside each
-// 16-lane row, then the two row swaps); every lane ends with the results.
+// Maximum over each 32-lane half of N values per lane (four DPP steps inside
+// each 16-lane row, then the swap between rows 0-1 and 2-3 of the half). The
+// callers' two halves hold the same values (after the half sums every lane
+// holds its position's full scores), so this is the maximum over the wave.
 __device__ __forceinline__ void wave_max4(float (&x)[4]) {
   float t[4];
   asm("s_nop 1\n\t"
@@ -421,19 +423,6 @@ __device__ __forceinline__ void wave_max4(float (&x)[4]) {
       "v_permlane16_swap_b32 %1, %5\n\t"
       "v_permlane16_swap_b32 %2, %6\n\t"
       "v_permlane16_swap_b32 %3, %7\n\t"
-      "v_max_f32 %0, %0, %4\n\t"
-      "v_max_f32 %1, %1, %5\n\t"
-      "v_max_f32 %2, %2, %6\n\t"
-      "v_max_f32 %3, %3, %7\n\t"
-      "v_mov_b32 %4, %0\n\t"
-      "v_mov_b32 %5, %1\n\t"
-      "v_mov_b32 %6, %2\n\t"
-      "v_mov_b32 %7, %3\n\t"
-      "s_nop 1\n\t"
-      "v_permlane32_swap_b32 %0, %4\n\t"
-      "v_permlane32_swap_b32 %1, %5\n\t"
-      "v_permlane32_swap_b32 %2, %6\n\t"
-      "v_permlane32_swap_b32 %3, %7\n\t"
       "v_max_f32 %0, %0, %4\n\t"
       "v_max_f32 %1, %1, %5\n\t"
       "v_max_f32 %2, %2, %6\n\t"
@@ -494,31 +483,6 @@ __device__ __forceinline__ void wave_max8(float (&x)[8]) {
       "v_permlane16_swap_b32 %5, %13\n\t"
       "v_permlane16_swap_b32 %6, %14\n\t"
       "v_permlane16_swap_b32 %7, %15\n\t"
-      "v_max_f32 %0, %0, %8\n\t"
-      "v_max_f32 %1, %1, %9\n\t"
-      "v_max_f32 %2, %2, %10\n\t"
-      "v_max_f32 %3, %3, %11\n\t"
-      "v_max_f32 %4, %4, %12\n\t"
-      "v_max_f32 %5, %5, %13\n\t"
-      "v_max_f32 %6, %6, %14\n\t"
-      "v_max_f32 %7, %7, %15\n\t"
-      "v_mov_b32 %8, %0\n\t"
-      "v_mov_b32 %9, %1\n\t"
-      "v_mov_b32 %10, %2\n\t"
-      "v_mov_b32 %11, %3\n\t"
-      "v_mov_b32 %12, %4\n\t"
-      "v_mov_b32 %13, %5\n\t"
-      "v_mov_b32 %14, %6\n\t"
-      "v_mov_b32 %15, %7\n\t"
-      "s_nop 1\n\t"
-      "v_permlane32_swap_b32 %0, %8\n\t"
-      "v_permlane32_swap_b32 %1, %9\n\t"
-      "v_permlane32_swap_b32 %2, %10\n\t"
-      "v_permlane32_swap_b32 %3, %11\n\t"
-      "v_permlane32_swap_b32 %4, %12\n\t"
-      "v_permlane32_swap_b32 %5, %13\n\t"
-      "v_permlane32_swap_b32 %6, %14\n\t"
-      "v_permlane32_swap_b32 %7, %15\n\t"
       "v_max_f32 %0, %0, %8\n\t"
       "v_max_f32 %1, %1, %9\n\t"
       "v_max_f32 %2, %2, %10\n\t"

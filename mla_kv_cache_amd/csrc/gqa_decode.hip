@@ -877,6 +877,18 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
       });
       // The K area is rewritten by the next tile's copy: all its reads are done.
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // Request this wave's next K tile of the item now, so that it overlaps
+      // the softmax and the V products below. First wait, in a form the
+      // compiler sees, for this tile's V rows (issued with its K): later
+      // waits it would place for them could not tell the new copies apart.
+      if (t0 + kWaves * TR < end) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __amdgpu_buffer_rsrc_t krn, vrn;
+        uint32_t toffn;
+        rsrc_at(b, j, n, t0 + kWaves * TR, krn, vrn, toffn);
+        copy_k(krn, toffn);
+        k_ahead = true;
+      }
       if constexpr (G == 1) half_sum1(s);
       else if constexpr (G == 2) half_sum2(s);
       else if constexpr (G == 4) half_sum4(s);

@@ -18,8 +18,9 @@
 // and 16 output tiles (256 AGPRs) for the whole partition.
 //
 // The latent tile (32 positions x 576) is copied from HBM straight into LDS
-// with global_load_lds (no register staging) into a ring of three buffers:
-// the copies of the next two tiles are in flight while one is computed. HBM
+// (buffer loads with the lds flag, no register staging) into a ring of four
+// buffers: the copies of the next three tiles are in flight while one is
+// computed, their blocks issued between the output products. HBM
 // sees every cached row of the partition once. Rows are 1152 bytes with
 // 16-byte chunks XOR-swizzled per row, which keeps both read patterns below
 // free of bank conflicts on the 64-bank LDS.
@@ -105,9 +106,9 @@ struct TileCopy {
   static constexpr int kBufBytes = kBlocks * 1024;
 };
 
-// Copy one latent tile (32 rows from byte offset `soff` of the buffer
-// `rsrc`) into an LDS buffer. Lane i of block k fills LDS chunk 64k + i =
-// (row, pc) from logical chunk pc ^ sw(row) of that row; voff[k] is that
+// Copy block k of a latent tile (32 rows from byte offset `soff` of the
+// buffer `rsrc`) into an LDS buffer. Lane i of block k fills LDS chunk 64k + i
+// = (row, pc) from logical chunk pc ^ sw(row) of that row; voff is that
 // chunk's byte offset within the tile (tile_voffsets). Rows at or past the
 // resource's num_records bytes arrive as zeros.
 //
@@ -115,21 +116,25 @@ struct TileCopy {
 // writes no register, only LDS, and M0 holds the block's LDS address (no
 // other code in these kernels uses M0). Written this way the compiler does not
 // insert a wait for the copy before every later LDS read (it cannot prove that
-// the reads touch another buffer); the kernel waits for the copy itself
-// (s_waitcnt vmcnt before the barrier that opens the tile).
+// the reads touch another buffer); the kernel waits for the copies itself
+// (s_waitcnt vmcnt before the barrier that opens a tile).
+template <int NWAVES>
+__device__ __forceinline__ void copy_block(unsigned char* buf, __amdgpu_buffer_rsrc_t rsrc, uint32_t soff,
+                                           uint32_t voff, int wave, int k) {
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)buf;
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + 1024u * (uint32_t)(wave + NWAVES * k));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               ::"s"(dst), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
 template <int NWAVES>
 __device__ __forceinline__ void copy_tile(unsigned char* buf, __amdgpu_buffer_rsrc_t rsrc, uint32_t soff,
                                           const uint32_t (&voff)[TileCopy<NWAVES>::kPerWave], int wave) {
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)buf;
 #pragma unroll
-  for (int k = 0; k < TileCopy<NWAVES>::kPerWave; ++k) {
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + 1024u * (uint32_t)(wave + NWAVES * k));
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 ::"s"(dst), "v"(voff[k]), "s"(rsrc), "s"(soff) : "memory");
-  }
+  for (int k = 0; k < TileCopy<NWAVES>::kPerWave; ++k) copy_block<NWAVES>(buf, rsrc, soff, voff[k], wave, k);
 }
 
-// Byte offsets within a tile of the chunks this lane copies (see copy_tile);
+// Byte offsets within a tile of the chunks this lane copies (see copy_block);
 // lanes of slack blocks past the tile read row 0 into the slack space.
 template <int NWAVES>
 __device__ __forceinline__ void tile_voffsets(uint32_t (&voff)[TileCopy<NWAVES>::kPerWave], int wave, int lane) {
@@ -142,16 +147,13 @@ __device__ __forceinline__ void tile_voffsets(uint32_t (&voff)[TileCopy<NWAVES>:
 }
 
 // Wait until this wave's copies of the current tile have landed while the
-// copies of the next tile (N of them, issued later) may still be in flight,
-// then barrier: afterwards every wave's copies of the current tile are in
-// LDS and every wave is done with the tile before it.
+// copies of the next two tiles (N of them, issued later) may still be in
+// flight, then barrier: afterwards every wave's copies of the current tile are
+// in LDS and every wave is done with the tile before it. The counter holds at
+// most 63; a smaller bound only waits longer.
 template <int N>
 __device__ __forceinline__ void wait_tile_barrier() {
-  if constexpr (N == 36) asm volatile("s_waitcnt vmcnt(36) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else static_assert(N == 9, "no wait defined for this copy count");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N > 63 ? 63 : N) : "memory");
 }
 
 // acc *= f on an accumulator tile that lives in AGPRs, in place, through one
@@ -181,6 +183,9 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float f) {
 // fragments and the accumulators).
 constexpr int kQkAhead = 6;
 constexpr int kPvAhead = 3;
+// Tile buffers in the ring: tile i sits in buffer i % 4, and the copy of tile
+// i + 3 goes into the buffer of tile i - 1.
+constexpr int kRing = 4;
 
 // One wave per 32 heads, each with the whole 576-wide score contraction and
 // all 512 output dims (see the file comment). NW waves (NW * 32 heads) share
@@ -198,7 +203,7 @@ void mla_partial_kernel(const MlaArgs a) {
   const int H = a.H, T_max = a.T_max, P = a.P, NP = a.NP;
   const float qk_scale_log2 = a.qk_scale_log2;
   using TC = TileCopy<NW>;
-  __shared__ __attribute__((aligned(1024))) unsigned char bufs[3][TC::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char bufs[kRing][TC::kBufBytes];
 
   // Work-group L of the 1-D grid serves (partition p, head block hb,
   // sequence b). Work-groups are handed to the 8 XCDs in turn (L % 8), each
@@ -253,8 +258,13 @@ void mla_partial_kernel(const MlaArgs a) {
       r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(lat), 0, 0, kBufWord3);
       soff = 0;
     } else if constexpr (PAGED) {
-      const int phys = min(max(a.block_table[(size_t)b * a.max_pages + (t0 >> a.page_shift)], 0),
-                           a.num_pages - 1);
+      // The table entry is read with a scalar load (waited for at once):
+      // as a vector load, the compiler's wait for it would also wait for
+      // every tile copy in flight, which it does not know about.
+      const int32_t* ent = a.block_table + (size_t)b * a.max_pages + (t0 >> a.page_shift);
+      int raw;
+      asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(raw) : "s"(ent) : "memory");
+      const int phys = min(max(raw, 0), a.num_pages - 1);
       const uint16_t* base = lat + ((size_t)phys * a.page_size + (t0 & (a.page_size - 1))) * kRow;
       r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, min(kTile, n - t0) * (kRow * 2),
                                             kBufWord3);
@@ -264,6 +274,17 @@ void mla_partial_kernel(const MlaArgs a) {
       soff = (uint32_t)t0 * (kRow * 2);
     }
   };
+
+  {  // the first three tiles, in flight together with the query loads
+    __amdgpu_buffer_rsrc_t r;
+    uint32_t soff;
+    tile_src(start, r, soff);
+    copy_tile<NW>(bufs[0], r, soff, voff, wave);
+    tile_src(start + kTile, r, soff);
+    copy_tile<NW>(bufs[1], r, soff, voff, wave);
+    tile_src(start + 2 * kTile, r, soff);
+    copy_tile<NW>(bufs[2], r, soff, voff, wave);
+  }
 
   // Query fragments for all 576 score dims.
   uint4 qf[kSteps];
@@ -275,21 +296,13 @@ void mla_partial_kernel(const MlaArgs a) {
       const int d = 16 * ks + 8 * half;
       qf[ks] = d < kDc ? ld16(qn + d) : ld16(qr + (d - kDc));
     }
-    // Wait for the query here, in a form the compiler's own wait counting
-    // sees (vmcnt(0), the other counters at maximum): otherwise it waits for
-    // them inside the tile loop with counts that also cover the tile copies
-    // in flight, which would stall every tile on its successors' copies.
+    // Wait for the query (and this wave's first copies) here, in a form the
+    // compiler's own wait counting sees (vmcnt(0), the other counters at
+    // maximum): otherwise it waits for the query inside the tile loop with
+    // counts that also cover the tile copies in flight, which would stall
+    // every tile on its successors' copies.
     __builtin_amdgcn_s_waitcnt(0x0F70);
   }
-  {
-    __amdgpu_buffer_rsrc_t r;
-    uint32_t soff;
-    tile_src(start, r, soff);
-    copy_tile<NW>(bufs[0], r, soff, voff, wave);
-    tile_src(start + kTile, r, soff);
-    copy_tile<NW>(bufs[1], r, soff, voff, wave);
-  }
-
   f32x16 acc[kOTiles];
 #pragma unroll
   for (int t = 0; t < kOTiles; ++t)
@@ -316,13 +329,13 @@ void mla_partial_kernel(const MlaArgs a) {
 
   auto tile = [&](const unsigned char* __restrict__ cur_b, unsigned char* __restrict__ nxt_b, int t0) {
     const uint16_t* cur = reinterpret_cast<const uint16_t*>(cur_b);
-    wait_tile_barrier<TC::kPerWave>();
-    {  // the copy of the tile after next (a null copy past the end)
-      __amdgpu_buffer_rsrc_t r2;
-      uint32_t soff2;
-      tile_src(t0 + 2 * kTile, r2, soff2);
-      copy_tile<NW>(nxt_b, r2, soff2, voff, wave);
-    }
+    wait_tile_barrier<(kRing - 2) * TC::kPerWave>();
+    // The copy of the tile three ahead (a null copy past the end) goes into
+    // the buffer of the tile before this one; its blocks are issued between
+    // the output products below.
+    __amdgpu_buffer_rsrc_t r3;
+    uint32_t soff3;
+    tile_src(t0 + 3 * kTile, r3, soff3);
 
     // ---- scores S^T = L . Q^T over all 576 dims
     f32x16 s;
@@ -405,6 +418,14 @@ void mla_partial_kernel(const MlaArgs a) {
         const uint16_t* phi = base_hi + 64 * (t >> 1) + poff[1][t & 1];
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)plo);
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)phi);
+        // Copy block j goes out after the reads of output step
+        // kPvAhead + 29 j / kPerWave: LDS reads do not cross the copies (asm
+        // statements), so each lands between two pairs of products and the
+        // copy path never stalls the wave for a whole tile's worth of copies.
+#pragma unroll
+        for (int j = 0; j < TC::kPerWave; ++j)
+          if (kPvAhead + (j * (2 * kOTiles - kPvAhead)) / TC::kPerWave == kOTiles * ks + t)
+            copy_block<NW>(nxt_b, r3, soff3, voff[j], wave, j);
         uint4 av;
         av.x = __builtin_bit_cast(uint2, lo).x;
         av.y = __builtin_bit_cast(uint2, lo).y;
@@ -426,15 +447,15 @@ void mla_partial_kernel(const MlaArgs a) {
     }
   };
 
-  // Tile i sits in buffer i % 3; the copy of tile i + 2 goes into the buffer
-  // of tile i - 1, which every wave has finished with at tile i's barrier.
+  // The copy of tile i + 3 goes into the buffer of tile i - 1, which every
+  // wave has finished with at tile i's barrier.
   int cur = 0;
   for (int t0 = start; t0 < end; t0 += kTile) {
-    const int nxt = cur == 0 ? 2 : cur - 1;
+    const int nxt = (cur + kRing - 1) & (kRing - 1);
     tile(bufs[cur], bufs[nxt], t0);
-    cur = cur == 2 ? 0 : cur + 1;
+    cur = (cur + 1) & (kRing - 1);
   }
-  // The copies issued during the last two tiles (zeros into free buffers)
+  // The copies issued during the last three tiles (zeros into free buffers)
   // land before the work-group can end.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 

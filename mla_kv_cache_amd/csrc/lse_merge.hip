@@ -168,6 +168,9 @@ __device__ __forceinline__ long long split_units(const int32_t* seq_lens, int b,
 // holding unit base + units - 1, leaving out work-groups whose run was empty
 // (only when U < NW). The merge itself is the same log-sum-exp regrouping as
 // for fixed partitions. One wave per row, four rows per work-group.
+// Slots per row whose partial rows the merge requests up front.
+constexpr int kPreSlots = 16;
+
 template <typename TO, int VW>
 __global__ __launch_bounds__(64 * kRowsPerGroup) void split_merge_kernel(
     const float* __restrict__ part_out, const float* __restrict__ part_lse,
@@ -206,6 +209,43 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void split_merge_kernel(
   const long long pi = (long long)b * h_kv + j;
   const int ns = w1 - w0 + 1;
   auto slot_row = [&](int s) { return ((size_t)(w0 + s + pi) * G + hh); };
+
+  // Common case: few slots and one Dv chunk per lane. The rows are requested
+  // together with the slot lse values (one lane per slot), not after the
+  // maximum and the sum, which saves one round trip to memory.
+  if (ns <= kPreSlots && Dv == 64 * VW) {
+    const int d0 = lane * VW;
+    // Slot `lane` is written when its work-group holds a unit (64-bit
+    // divisions: evaluated once per slot, then shared as a mask).
+    const bool hl = lane < ns && (U >= NW || held(w0 + lane));
+    const uint64_t hm = __ballot(hl);
+    typename V::type x[kPreSlots];
+#pragma unroll
+    for (int s = 0; s < kPreSlots; ++s)
+      if ((hm >> s) & 1) x[s] = *reinterpret_cast<const typename V::type*>(part_out + slot_row(s) * Dv + d0);
+    const float ls = hl ? part_lse[slot_row(lane)] : kNegInf;
+    const float Mx = wave_max(ls);
+    const float e = ls == kNegInf ? 0.f : fast_exp2(ls - Mx);
+    const float inv = 1.f / wave_sum(e);
+    float acc[4][VW];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < VW; ++i) acc[u][i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < kPreSlots; ++s) {
+      if ((hm >> s) & 1) {
+        const float w = __shfl(e, s, 64) * inv;
+#pragma unroll
+        for (int i = 0; i < VW; ++i) acc[s % 4][i] = fmaf(w, V::get(x[s], i), acc[s % 4][i]);
+      }
+    }
+    float r[VW];
+#pragma unroll
+    for (int i = 0; i < VW; ++i) r[i] = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+    store_out<VW>(o + d0, r);
+    return;
+  }
 
   float M = kNegInf;
   for (int s = lane; s < ns; s += 64)

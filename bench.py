@@ -332,7 +332,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library runs on a single MI355X and has no "
-              "multi-GPU path (see DESIGN.md for how it would shard). Use --gpus 1.", file=sys.stderr)
+              "multi-GPU path. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -19,7 +19,7 @@ Sources (page title -- section):
   average of latents; a small decoupled rotary key is cached beside the
   latent and enters only the score).
 
-Readings of points the pages leave open (each listed in the design doc):
+Readings of points the pages leave open:
 
 * Decode attends over every cached position t < n with no mask: the newest
   token is already in the cache (append-then-attend, as in the MLA decode

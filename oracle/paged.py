@@ -8,7 +8,7 @@ Source (page title -- section): "Attention variants: MQA, GQA, and MLA" --
 pages that are allocated like virtual memory and may be shared between
 sequences with a common prefix.
 
-Layout (a reading: the page names no layout; listed in the design doc):
+Layout (a reading: the pages name no layout):
 
 * GQA: ``k_pages``, ``v_pages`` [num_pages, h_kv, page_size, D]; logical
   position t of sequence b lives in physical page ``block_table[b, t //

@@ -12,7 +12,7 @@ Sources (page title -- section):
   and values" (decode sketch): the new token's latent is concatenated to the
   latent cache, and the scores and the average run over the extended cache.
 
-Readings of points the pages leave open (each listed in the design doc):
+Readings of points the pages leave open:
 
 * ``seq_lens[b]`` holds the number of cached positions *before* the step;
   the new row goes to position ``pos = max(seq_lens[b], 0)`` and the step

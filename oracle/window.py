@@ -12,7 +12,7 @@ Sources (page title -- section):
 * "Attention variants: MQA, GQA, and MLA" -- "Traps and misconceptions": the
   window is an axis independent of KV-head sharing (Mistral uses both).
 
-Reading of what the pages leave open (listed in the design doc): a decode token at
+Reading of what the pages leave open: a decode token at
 sequence length n attends over the last ``window`` cached positions,
 t in [max(0, n - window), n); ``window >= n`` is the full decode. Everything
 else (group map, scale, clamping of n, padding never read) is as in

@@ -50,10 +50,23 @@ __device__ __forceinline__ void store_out(float* o, const float (&x)[VW]) {
 #pragma unroll
   for (int i = 0; i < VW; ++i) o[i] = x[i];
 }
+// bf16 output: the merged rows are read by the caller's next kernel, not by
+// this step's, so they are written non-temporally; cached dirty copies were
+// written back while the next decode kernel streamed its cache.
 template <int VW>
 __device__ __forceinline__ void store_out(uint16_t* o, const float (&x)[VW]) {
+  if constexpr (VW == 4) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = {(uint32_t)f32_to_bf16_rne(x[0]) | ((uint32_t)f32_to_bf16_rne(x[1]) << 16),
+                     (uint32_t)f32_to_bf16_rne(x[2]) | ((uint32_t)f32_to_bf16_rne(x[3]) << 16)};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(o));
+  } else if constexpr (VW == 2) {
+    __builtin_nontemporal_store((uint32_t)f32_to_bf16_rne(x[0]) | ((uint32_t)f32_to_bf16_rne(x[1]) << 16),
+                                reinterpret_cast<uint32_t*>(o));
+  } else {
 #pragma unroll
-  for (int i = 0; i < VW; ++i) o[i] = f32_to_bf16_rne(x[i]);
+    for (int i = 0; i < VW; ++i) __builtin_nontemporal_store(f32_to_bf16_rne(x[i]), o + i);
+  }
 }
 
 template <typename TO, int VW>

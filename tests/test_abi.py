@@ -66,6 +66,12 @@ def test_kv_helper_reproduces_page_numbers(lib):
         assert lib.attn_mla_cache_bytes(*case["args"]) == case["elements"], case["cite"]
 
 
+def test_mla_helper_reproduces_scaled_page_numbers(lib):
+    data = json.load(open(os.path.join(ROOT, "tests", "golden", "cache_bytes.json")))
+    for case in data["mla_bytes"]:
+        assert lib.attn_mla_cache_bytes(*case["args"]) == case["bytes"], case["cite"]
+
+
 def test_helpers_agree_with_oracle_and_saturate(lib):
     rng = random.Random(0)
     for _ in range(500):

@@ -61,6 +61,20 @@ def test_mla_cache_elements_match_pages():
             assert 2 * case["gqa_equiv_kv_heads"] * case["head_dim"] == case["elements"]
 
 
+def test_mla_cache_bytes_match_pages():
+    """The MLA row per token scaled by bytes per value, layers, tokens and
+    sequences: each factor differs from 1 in some case, so dropping any fails."""
+    data = _load("cache_bytes.json")
+    for i in (0, 3, 4, 5):                                  # layers, tokens, sequences, bytes
+        assert any(c["args"][i] != 1 for c in data["mla_bytes"])
+    for case in data["mla_bytes"]:
+        assert oracle.mla_cache_bytes(*case["args"]) == case["bytes"], case["cite"]
+        if "mha_args" in case:
+            mha = oracle.kv_cache_bytes(*case["mha_args"])
+            assert mha == case["mha_bytes"]
+            assert case["bytes"] < mha / 3                  # that notebook's own check
+
+
 def test_cache_ratios_match_pages():
     data = _load("cache_bytes.json")
     nb = data["ratios"][0]
@@ -84,18 +98,20 @@ def _sdpa_decode_rows(q, k, v, scale=None):
 
 
 def test_gqa_matches_sdpa_causal_rows():
-    """The first page's library check shape (B=2, Hq=8, Hkv=2, T=64, d=32, seed 0, float64).
+    """Causal prefill attention through PyTorch's CPU SDPA with native GQA head
+    sharing, in float64 ("Attention variants: MQA, GQA, and MLA", section
+    "Against the real libraries" checks its own implementation this way).
 
     Row t of causal attention over T positions is a decode step that attends
-    over positions 0..t; every row pins the oracle with n = t + 1.
+    over positions 0..t; every row pins the oracle with n = t + 1. Shapes and
+    seed are this test's own: 3 KV heads shared by 12 query heads.
     """
-    torch.manual_seed(0)
-    B, Hq, Hkv, T, d = 2, 8, 2, 64, 32
-    q = torch.randn(B, Hq, T, d, dtype=torch.float64)
-    k = torch.randn(B, Hkv, T, d, dtype=torch.float64)
-    v = torch.randn(B, Hkv, T, d, dtype=torch.float64)
+    B, Hq, Hkv, T, d = 3, 12, 3, 50, 24
+    q = _rand((B, Hq, T, d), 123)
+    k = _rand((B, Hkv, T, d), 124)
+    v = _rand((B, Hkv, T, d), 125)
     ref = _sdpa_decode_rows(q, k, v)
-    for t in [0, 1, 2, 17, 40, T - 1]:
+    for t in [0, 1, 2, 13, 31, T - 1]:
         got = oracle.decode_gqa(q[:, :, t], k, v, [t + 1] * B, 1.0 / math.sqrt(d))
         assert np.abs(got - ref[:, :, t].numpy()).max() <= 1e-12
 
@@ -229,6 +245,31 @@ def test_weights_are_a_distribution():
     for W in oracle.decode_gqa_weights(q, k, [40, 13, 1], 0.31):
         assert (W >= 0).all()
         assert np.abs(W.sum(axis=1) - 1.0).max() <= 1e-14
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(6, 3), (8, 1), (4, 4), (12, 2)])
+def test_weights_equal_sdpa_with_one_hot_values(h_q, h_kv):
+    """The weights against a library routine: with the identity matrix as the
+    values (value of position t = unit vector e_t), SDPA's output row is the
+    softmax weight vector itself. Group map, scale and lengths all enter."""
+    B, T, d = 3, 23, 7
+    q = _rand((B, h_q, d), 160 + h_q)
+    k = _rand((B, h_kv, T, d), 170 + h_kv)
+    lens = [23, 9, 1]
+    got = oracle.decode_gqa_weights(q, k, lens, 0.43)
+    for b, n in enumerate(lens):
+        eye = torch.eye(n, dtype=torch.float64).expand(1, h_kv, n, n)
+        ref = F.scaled_dot_product_attention(q[b:b + 1, :, None], k[b:b + 1, :, :n], eye,
+                                             scale=0.43, enable_gqa=True)[0, :, 0]
+        assert got[b].shape == (h_q, n)
+        assert np.abs(got[b] - ref.numpy()).max() <= 1e-14
+    # and weights @ V is the decode output
+    v = _rand((B, h_kv, T, 5), 180)
+    out = oracle.decode_gqa(q, k, v, lens, 0.43)
+    g = h_q // h_kv
+    for b, n in enumerate(lens):
+        for i in range(h_q):
+            assert np.abs(got[b][i] @ v[b, i // g, :n].numpy() - out[b, i]).max() <= 1e-14
 
 
 def test_position_and_batch_permutations():

@@ -59,6 +59,12 @@
  *   cut points then depend on the sequence lengths and on the device's
  *   compute-unit count; on one device the output is still bit-identical
  *   from run to run.
+ * - Host state: the library keeps, per device index, the device's compute-
+ *   unit count, and per process the resident work-groups per compute unit of
+ *   each persistent kernel (a property of the kernel on gfx950), both read
+ *   once from the HIP runtime on first use (thread-safe, written once).
+ *   Nothing else persists between calls, and no call depends on a previous
+ *   one.
  */
 #ifndef ATTN_DECODE_H
 #define ATTN_DECODE_H
@@ -251,9 +257,12 @@ int attn_decode_merge(const float* part_out, const float* part_lse, const int32_
  * seq_lens        int32 [B]
  * out             [B, H, d_c]          bf16: weighted average of latents
  * s_t = scale * (<q_nope, latent[t, :d_c]> + <q_rope, latent[t, d_c:]>).
- * Supported: (d_c, d_r) = (512, 64); H a multiple of 32 up to 128 (MFMA tiles of
- * 32 heads); bf16 only. The rotary key is used as stored: rotating it and
- * q_rope by position is the caller's job.
+ * Supported: (d_c, d_r) = (512, 64); H in {32, 64, 96, 128} or any multiple of
+ * 128 (MFMA tiles of 32 heads, one work-group per block of up to 128 heads);
+ * bf16 only; one sequence's rows, T_max * (d_c + d_r) * 2 bytes, below 2 GiB
+ * (ATTN_ERR_UNSUPPORTED otherwise: the kernels address them with 32-bit
+ * offsets). The rotary key is used as stored: rotating it and q_rope by
+ * position is the caller's job.
  */
 int attn_decode_mla_plan(int B, int H, int d_c, int d_r, int T_max,
                          int* partition_size, int* num_partitions, size_t* workspace_bytes);

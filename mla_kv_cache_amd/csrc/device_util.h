@@ -100,9 +100,14 @@ __device__ __forceinline__ float wave_sum(float x) {
 // compiler does not wait for the copy before unrelated LDS reads; the caller
 // waits with s_waitcnt vmcnt. The instruction writes no register, only LDS;
 // M0 carries the LDS address and no other code in these kernels uses M0.
+// M0 is a reserved register to the compiler, which warns when an assembly
+// block names it as clobbered; the clobber is kept so that the compiler never
+// assumes a value of its own survives the block.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void copy16_to_lds(uint32_t lds_base, const void* src) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(src) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(src) : "memory", "m0");
 }
 
 // Same copy with a wave-uniform base address (scalar register pair) and a
@@ -116,8 +121,9 @@ __device__ __forceinline__ void copy16_to_lds_sbase(uint32_t lds_base, const voi
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32));
   const uint64_t sbu = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(base), "v"(voff), "s"(sbu) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(base), "v"(voff), "s"(sbu) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // 16-byte vector store. Every call site guarantees 16-byte alignment.
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }

@@ -296,17 +296,22 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // Hand-scheduled blocks of DPP arithmetic (inline assembly). The compiler
-// inserts the wait states that gfx950 needs between dependent instructions
-// for the code it generates, but it cannot see into inline assembly, so each
-// block carries its own, as measured on the part:
-//  * a VALU write followed by a DPP read of that VGPR needs two wait states;
-//  * a VALU write followed by v_permlane16/32_swap reading it needs two;
-//  * a v_dot2c_f32_bf16 result read by any other VALU instruction needs
-//    three, while a following v_dot2c accumulating into the same register
-//    needs none.
+// inserts the wait states gfx950 needs between dependent instructions for the
+// code it generates, but it cannot see into inline assembly, so each block
+// carries its own. The requirements are those of the wait-state table in
+// AMD's CDNA3 / CDNA4 instruction-set reference guides ("Manually Inserted
+// Wait States (NOPs)"), which LLVM's AMDGPU hazard recognizer also enforces
+// for gfx940 / gfx950 code:
+//  * a VALU write of a VGPR followed by a DPP read of that VGPR: two wait states;
+//  * a VALU write of a VGPR followed by v_permlane16/32_swap reading it (new
+//    in CDNA4): two;
+//  * a dot-product (v_dot2c_f32_bf16) result read by any other VALU
+//    instruction: three, while the same dot instruction accumulating into
+//    that register needs none.
 // Every block therefore opens with s_nop 1 (covering whatever the compiler
 // wrote just before) and closes with enough wait states for whatever the
-// compiler reads just after; inside a block the spacing is explicit.
+// compiler reads just after; inside a block the spacing is explicit. A CPU
+// test compiles the kernels and scans the assembly for these rules.
 
 // acc[h] += dot(q_h, k) over the four bf16 pairs of one 16-byte K chunk, for
 // G heads: query word e of the chunk for head h is the value that lane L0 + e
@@ -741,6 +746,10 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
     const int lc = pc ^ ((RPC * mm + rl) % CH);
     kvoff[mm] = (uint32_t)(rl * D + lc * 8) * 2u;
   }
+  // (M0 is reserved to the compiler, which warns about the clobber; it is
+  // kept so that no value of the compiler's own is assumed to survive.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
   auto copy_k = [&](const __amdgpu_buffer_rsrc_t& kr, uint32_t tile_off) {
     const uint32_t dst = kt_lds;
 #pragma unroll
@@ -748,9 +757,10 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
       const uint32_t soff = tile_off + 1024u * i;
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                    ::"s"(dst + 1024u * i), "v"(kvoff[i % KPER]), "s"(kr), "s"(soff)
-                   : "memory");
+                   : "memory", "m0");
     }
   };
+#pragma clang diagnostic pop
   // V rows -> registers (row layout): load i brings rows i*RPI .. i*RPI+RPI-1.
   const uint32_t vvoff = (uint32_t)(rr * D + c * 8) * 2u;
   auto load_v = [&](const __amdgpu_buffer_rsrc_t& vr_, uint32_t tile_off, int i) {
@@ -1099,17 +1109,12 @@ hipError_t launch_one(const GqaArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-#ifndef ATTN_PO_MIN_GROUP
-#define ATTN_PO_MIN_GROUP 1
-#endif
-// Smallest group size served by the position-per-lane kernel (bf16 only).
-constexpr int kPoMinGroup = ATTN_PO_MIN_GROUP;
 template <class E, int D>
 hipError_t launch_d(int G, const GqaArgs& a, hipStream_t s) {
   if constexpr (sizeof(typename E::storage) == 2) {
     // The position-per-lane kernel reads a paged cache one 32-row tile at a time.
     const bool tiles_fit = a.block_table == nullptr || a.page_size % kPoRows == 0;
-    if (G >= kPoMinGroup && tiles_fit) {
+    if (tiles_fit) {
       switch (G) {
         case 1: return launch_po<D, 1>(a, s);
         case 2: return launch_po<D, 2>(a, s);
@@ -1186,7 +1191,7 @@ hipError_t launch_gqa_split(int D, int group, const GqaArgs& a, int groups, hipS
 }
 
 bool gqa_persistent(int dt, int D, int group) {
-  return dt == 1 && (D == 64 || D == 128) && group >= kPoMinGroup && group <= 8 && (group & (group - 1)) == 0;
+  return dt == 1 && (D == 64 || D == 128) && group >= 1 && group <= 8 && (group & (group - 1)) == 0;
 }
 
 bool gqa_supported(int dt, int D, int group) {

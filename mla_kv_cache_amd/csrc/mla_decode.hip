@@ -118,14 +118,20 @@ struct TileCopy {
 // insert a wait for the copy before every later LDS read (it cannot prove that
 // the reads touch another buffer); the kernel waits for the copies itself
 // (s_waitcnt vmcnt before the barrier that opens a tile).
+// M0 is a reserved register to the compiler, which warns when an assembly
+// block names it as clobbered; the clobber is kept so that the compiler never
+// assumes a value of its own survives the block.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 template <int NWAVES>
 __device__ __forceinline__ void copy_block(unsigned char* buf, __amdgpu_buffer_rsrc_t rsrc, uint32_t soff,
                                            uint32_t voff, int wave, int k) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)buf;
   const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + 1024u * (uint32_t)(wave + NWAVES * k));
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               ::"s"(dst), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+               ::"s"(dst), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 template <int NWAVES>
 __device__ __forceinline__ void copy_tile(unsigned char* buf, __amdgpu_buffer_rsrc_t rsrc, uint32_t soff,

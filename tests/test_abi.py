@@ -163,6 +163,12 @@ def test_mla_argument_checks(lib):
     assert call(wsb=64) == WORKSPACE
     assert call(out=P16c) == INVALID                  # output overlaps the latent cache
     assert call(lat=ctypes.c_void_p((1 << 34) + 4)) == UNSUPPORTED
+    # one sequence's rows must stay below 2 GiB (32-bit offsets in the kernels)
+    big = (1 << 31) // 1152 + 1
+    assert call(B=1, T=big) == UNSUPPORTED
+    assert call(B=1, T=big - 1, wsb=0) == WORKSPACE    # the shape passes; stops at the workspace
+    assert lib.attn_decode_mla_plan(1, 128, 512, 64, big, None, None, None) == UNSUPPORTED
+    assert lib.attn_decode_mla_plan(1, 128, 512, 64, big - 1, None, None, None) == OK
     P, NP, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()
     assert lib.attn_decode_mla_plan(64, 128, 512, 64, 4096, ctypes.byref(P), ctypes.byref(NP),
                                     ctypes.byref(ws)) == OK

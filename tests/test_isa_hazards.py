@@ -1,21 +1,31 @@
-"""Wait-state rules around the hand-scheduled assembly blocks (CPU only).
+"""Wait-state rules around the hand-scheduled assembly blocks, and the use of M0 (CPU only).
 
 The GQA kernel issues some DPP arithmetic as inline assembly. The compiler
 inserts the wait states gfx950 needs between dependent instructions of the
 code it generates, but not across the boundary of an assembly block. This
 test compiles the kernels to gfx950 assembly and scans it linearly for the
-rules measured on the part:
+rules that apply to those blocks. The rules are the CDNA wait-state
+requirements as AMD documents them (the "Manually Inserted Wait States
+(NOPs)" table of the CDNA3 / CDNA4 instruction-set reference guides) and as
+LLVM's AMDGPU hazard recognizer enforces them for gfx940 / gfx950 code:
 
 * a VALU instruction writes a VGPR, then a DPP instruction reads it as its
   lane-shuffled operand (src0): at least 2 wait states in between;
-* a VALU instruction writes a VGPR, then v_permlane16/32_swap reads it: at
-  least 2 wait states;
-* v_dot2c_f32_bf16 writes a VGPR, then another VALU instruction (not a
-  v_dot2c accumulating into the same register) reads it: at least 3.
+* a VALU instruction writes a VGPR, then v_permlane16/32_swap (new in CDNA4)
+  reads it: at least 2 wait states;
+* a dot-product instruction (v_dot2c_f32_bf16) writes a VGPR, then another
+  VALU instruction reads it: at least 3 wait states; none are needed when the
+  reader is the same dot instruction accumulating into that register.
 
 ``s_nop N`` counts N + 1 wait states, any other instruction one. The scan
 ignores branches (it follows program order), which covers every block the
 assembly helpers emit: each one opens and closes with its own wait states.
+
+M0: the direct-to-LDS copies are assembly blocks that write M0 (the LDS
+address) and issue the copy right after. The compiler must not read M0 for
+anything of its own in these kernels; the scan checks that every instruction
+naming M0 is one of those writes, that each write is followed at once by its
+copy, and that no instruction that reads M0 implicitly appears elsewhere.
 """
 
 from __future__ import annotations
@@ -115,6 +125,54 @@ def _violations(lines: list[str]) -> list[str]:
                     ws += 1
                 j += 1
     return bad
+
+
+# Instructions that read M0 without naming it (gfx9 family).
+_M0_IMPLICIT = ("s_movrel", "v_movrel", "s_sendmsg", "ds_gws", "v_interp", "ds_ordered_count",
+                "ds_append", "ds_consume", "s_ttracedata")
+
+
+def _is_lds_copy(t: str) -> bool:
+    op = t.split()[0]
+    return ((op.startswith("buffer_load") and (t.endswith(" lds") or " lds " in t))
+            or op.startswith(("global_load_lds", "scratch_load_lds")))
+
+
+def _m0_violations(lines: list[str]) -> list[str]:
+    bad = []
+    ins = [t for t in lines if _is_instr(t)]
+    for i, t in enumerate(ins):
+        op = t.split()[0]
+        m0_write = re.match(r"s_mov_b32 m0, s\d+$", t) is not None
+        if re.search(r"\bm0\b", t) and not m0_write:
+            bad.append(f"names m0: {t}")
+        if m0_write and not (i + 1 < len(ins) and _is_lds_copy(ins[i + 1])):
+            bad.append(f"m0 write not followed by its copy: {t}")
+        if _is_lds_copy(t) and not (i > 0 and re.match(r"s_mov_b32 m0, s\d+$", ins[i - 1])):
+            bad.append(f"copy without its m0 write: {t}")
+        if op.startswith(_M0_IMPLICIT):
+            bad.append(f"reads m0 implicitly: {t}")
+    return bad
+
+
+@pytest.mark.parametrize("name", ["gqa_decode.hip", "mla_decode.hip", "lse_merge.hip", "mla_absorb.hip"])
+def test_m0_is_only_used_by_the_copy_blocks(name, tmp_path):
+    lines = _assembly(os.path.join(CSRC, name), tmp_path)
+    bad = _m0_violations(lines)
+    assert not bad, f"{len(bad)} M0 uses outside the copy blocks, first: " + "; ".join(bad[:5])
+
+
+def test_m0_scanner_catches_planted_uses():
+    lines = [
+        "s_mov_b32 m0, s4",
+        "buffer_load_dwordx4 v1, s[8:11], s12 offen lds",
+        "s_mov_b32 m0, s5",                      # not followed by a copy
+        "v_mov_b32 v2, v3",
+        "global_load_lds_dwordx4 v4, off",       # no m0 write right before
+        "v_readlane_b32 s6, v7, m0",             # the compiler reading m0
+        "s_movrels_b32 s1, s2",                  # implicit reader
+    ]
+    assert len(_m0_violations(lines)) == 4
 
 
 @pytest.mark.parametrize("name", ["gqa_decode.hip", "mla_decode.hip", "lse_merge.hip"])

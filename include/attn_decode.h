@@ -85,7 +85,15 @@ typedef enum {
   ATTN_ERR_HIP = -4           /* a kernel launch reported an error */
 } attn_status;
 
+/* Storage type of q, the caches and out. C callers may pass any int: values
+ * other than these two are rejected (ATTN_ERR_UNSUPPORTED). The C++ view gives
+ * the enumeration a fixed underlying int, so that such a value is a valid
+ * object to check rather than undefined behaviour (same ABI as the C view). */
+#ifdef __cplusplus
+typedef enum attn_dtype_e : int { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+#else
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+#endif
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* attn_status_str(int status);

@@ -55,6 +55,8 @@ int check_gqa_shape(const GqaShape& s) {
   if (s.T_max > kMaxTmax || s.B > kMaxGridYZ || s.h_kv > kMaxGridYZ) return ATTN_ERR_INVALID_ARG;
   if (int64_t(s.B) * s.h_kv * s.T_max * s.D >= kMaxElems) return ATTN_ERR_INVALID_ARG;
   if (int64_t(s.B) * s.h_q >= (int64_t(1) << 31)) return ATTN_ERR_INVALID_ARG;
+  // The generic kernel's grid has h_kv * max(1, g / 16) rows in its second dimension.
+  if (int64_t(s.h_kv) * std::max(1, s.h_q / s.h_kv / 16) > kMaxGridYZ) return ATTN_ERR_INVALID_ARG;
   if (s.dt != ATTN_F32 && s.dt != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (!attn::gqa_supported(int(s.dt), s.D, s.h_q / s.h_kv)) return ATTN_ERR_UNSUPPORTED;
   // The kernels address one (sequence, KV head) slab with 32-bit byte offsets.
@@ -71,7 +73,8 @@ int check_gqa_shape(const GqaShape& s) {
 // kernel aims for about 8192 work-groups (32 per CU).
 int gqa_auto_partition(const GqaShape& s) {
   const int64_t pairs = int64_t(s.B) * s.h_kv;
-  const int64_t target = attn::gqa_persistent(int(s.dt), s.D, s.h_q / s.h_kv) ? 2048 : 8192;
+  const int G = s.h_q / s.h_kv;
+  const int64_t target = attn::gqa_persistent(int(s.dt), s.D, G) || attn::gqa_matrix(int(s.dt), s.D, G) ? 2048 : 8192;
   const int64_t want = (int64_t(s.T_max) * pairs + target - 1) / target;
   int P = 512;
   while (P < want && P < 4096) P <<= 1;
@@ -86,7 +89,8 @@ size_t partial_bytes(int64_t rows, int NP, int Dv) {
 // its workspace, one partial per slot (work-groups + B * h_kv slots of G heads).
 int gqa_split_groups(const GqaShape& s) {
   const int G = s.h_q / s.h_kv;
-  return attn::gqa_persistent(int(s.dt), s.D, G) ? attn::gqa_split_groups(s.D, G) : 0;
+  return attn::gqa_persistent(int(s.dt), s.D, G) || attn::gqa_matrix(int(s.dt), s.D, G)
+             ? attn::gqa_split_groups(s.D, G) : 0;
 }
 size_t split_bytes(const GqaShape& s, int groups) {
   return partial_bytes((int64_t(groups) + int64_t(s.B) * s.h_kv) * (s.h_q / s.h_kv), 1, s.D);

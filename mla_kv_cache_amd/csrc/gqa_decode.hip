@@ -35,6 +35,7 @@
 
 #include "device_util.h"
 #include "launch.h"
+#include "split_items.h"
 
 namespace attn {
 namespace {
@@ -92,7 +93,11 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const GqaArgs a) 
   const int h_kv = a.h_kv, T_max = a.T_max, P = a.P, NP = a.NP;
   const float qk_scale_log2 = a.qk_scale_log2;
 
-  const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  // Groups above G heads are taken in head_chunks work-groups of G heads each
+  // (blockIdx.y = KV head * head_chunks + chunk); each reads the group's K/V rows.
+  const int chunks = a.head_chunks;
+  const int p = blockIdx.x, j = blockIdx.y / chunks, hc = blockIdx.y % chunks, b = blockIdx.z;
+  const int GG = G * chunks;  // query heads per KV head
   const int len0 = a.seq_lens[b];
   const int n = attended_len(len0, a.k_new ? 1 : 0, T_max);
   const int start = window_lo(n, a.window) + p * P;
@@ -110,10 +115,10 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const GqaArgs a) 
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rr = lane / LPR, c = lane % LPR;
-  const int H = h_kv * G;
+  const int H = h_kv * GG;
 
   uint4 qv[G];
-  const typename E::storage* qrow = q + ((size_t)b * H + (size_t)j * G) * D + c * EPL;
+  const typename E::storage* qrow = q + ((size_t)b * H + (size_t)j * GG + (size_t)hc * G) * D + c * EPL;
 #pragma unroll
   for (int h = 0; h < G; ++h) qv[h] = ld16(qrow + (size_t)h * D);
 
@@ -253,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const GqaArgs a) 
       L += sm_l[w][h] * f;
       A += sm_acc[w][h][d] * f;
     }
-    const size_t row = ((size_t)b * H + (size_t)j * G + h) * NP + p;
+    const size_t row = ((size_t)b * H + (size_t)j * GG + (size_t)hc * G + h) * NP + p;
     part_out[row * D + d] = A / L;
     if (d == 0) part_lse[row] = M + fast_log2(L);
   }
@@ -264,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const GqaArgs a) 
 //
 // The kernel is persistent: as many work-groups as the device holds at once
 // take equal runs of the non-empty (sequence, KV head, partition) items
-// (ItemRun below), so a ragged batch leaves no CU idle. Within an item the 4
+// (items::ItemRun in split_items.h), so a ragged batch leaves no CU idle. Within an item the 4
 // waves take 32-position tiles in turn. For a tile:
 //  * K rows go straight from HBM into the wave's own LDS area (direct copy,
 //    16 bytes per lane per instruction). Within each row the 16-byte chunks
@@ -595,104 +600,6 @@ __device__ __forceinline__ void half_sum8(float (&x)[8]) {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Work items of the persistent partial kernel: (sequence b, KV head j,
-// partition p) for every partition that holds at least one attended
-// position, numbered sequence-major (b, then j, then p). Work-group w of G
-// takes the contiguous run [w * N / G, (w + 1) * N / G) of the N items, so
-// every work-group gets the same number of partitions (give or take one)
-// whatever the mix of sequence lengths, and consecutive items mostly share
-// one query and one KV head.
-//
-// Split mode: the items are units of kSplitUnit positions (one 32-row tile
-// per wave), and a work-group treats the consecutive units of its run that
-// belong to one (b, j) as one segment, with one partial output. Every
-// work-group then streams the same number of units (give or take one), and
-// a (b, j) row is split between work-groups only where a run boundary falls.
-// The partial of work-group w's segment of pair (b, j) goes to slot
-// w + b * h_kv + j: along a run both w and the pair index only grow, so the
-// slots are distinct, and the segments of one pair sit in consecutive slots
-// (those of the work-groups whose run meets its units).
-struct ItemRun {
-  long long left;  // items still to do, the current one included
-  int b, j, p;     // current item
-  int np;          // partitions of sequence b
-};
-
-__device__ __forceinline__ int partitions_of(const GqaArgs& a, int b) {
-  const int n = attended_len(a.seq_lens[b], a.k_new ? 1 : 0, a.T_max);
-  return (int)(((long long)n - window_lo(n, a.window) + a.P - 1) / a.P);
-}
-
-__device__ __forceinline__ long long wave_sum_ll(long long x) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
-
-__device__ __forceinline__ long long wave_incl_scan_ll(long long x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const long long y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
-
-__device__ __forceinline__ long long uniform_ll(long long x) {
-  const uint64_t u = (uint64_t)x;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-  return (long long)(((uint64_t)hi << 32) | lo);
-}
-
-// This work-group's first item and item count. Every wave computes the same
-// (uniform) answer from the sequence lengths, 64 sequences at a time.
-__device__ ItemRun first_item(const GqaArgs& a) {
-  const int lane = threadIdx.x & 63;
-  ItemRun r{0, 0, 0, 0, 0};
-  long long total = 0;
-  for (int b0 = 0; b0 < a.B; b0 += 64) {
-    const int b = b0 + lane;
-    total += wave_sum_ll(b < a.B ? (long long)partitions_of(a, b) : 0);
-  }
-  total = uniform_ll(total * a.h_kv);
-  const long long lo = total * blockIdx.x / gridDim.x;
-  const long long hi = total * (blockIdx.x + 1) / gridDim.x;
-  if (hi <= lo) return r;
-  long long base = 0;
-  for (int b0 = 0; b0 < a.B; b0 += 64) {
-    const int b = b0 + lane;
-    const int np = b < a.B ? partitions_of(a, b) : 0;
-    const long long cnt = (long long)np * a.h_kv;
-    const long long incl = base + wave_incl_scan_ll(cnt, lane);
-    const uint64_t hit = __ballot(incl > lo);
-    if (hit) {
-      const int l0 = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
-      const long long excl = uniform_ll(__shfl(incl - cnt, l0, 64));
-      r.np = __builtin_amdgcn_readfirstlane(__shfl(np, l0, 64));
-      r.b = b0 + l0;
-      const long long off = lo - excl;
-      r.j = (int)(off / r.np);
-      r.p = (int)(off % r.np);
-      r.left = hi - lo;
-      return r;
-    }
-    base = uniform_ll(__shfl(incl, 63, 64));
-  }
-  return r;
-}
-
-// The item after the current one (sequences without partitions are skipped).
-__device__ __forceinline__ void next_item(ItemRun& r, const GqaArgs& a) {
-  if (++r.p < r.np) return;
-  r.p = 0;
-  if (++r.j < a.h_kv) return;
-  r.j = 0;
-  do {
-    ++r.b;
-  } while (r.b < a.B && (r.np = partitions_of(a, r.b)) == 0);
-}
-
 template <int D, int G, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs a) {
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
@@ -801,7 +708,7 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
   // requested before the previous item's combine.
   bool k_ahead = false;
 
-  for (ItemRun run = first_item(a); run.left > 0 && run.b < a.B;) {
+  for (items::ItemRun run = items::first_item(a); run.left > 0 && run.b < a.B;) {
     const int b = run.b, j = run.j, p = run.p;
     // Units (or partitions) of (b, j) this item covers: split mode takes all
     // of the run's remaining units of the pair at once.
@@ -976,11 +883,11 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
     // Request the K rows of this wave's first tile of the next item now, so
     // the copy overlaps the combine below (not in a decode step, whose next
     // item may first have to write its new row).
-    ItemRun nrun = run;
+    items::ItemRun nrun = run;
     bool have_next = run.left > len;
     if (have_next) {
       nrun.p = run.p + len - 1;
-      next_item(nrun, a);
+      items::next_item(nrun, a);
       have_next = nrun.b < a.B;
     }
     if (have_next && !a.k_new) {
@@ -1104,15 +1011,19 @@ int split_groups_dg() {
 }
 
 template <class E, int D, int G>
-hipError_t launch_one(const GqaArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((gqa_partial_kernel<E, D, G>), dim3(a.NP, a.h_kv, a.B), dim3(kThreads), 0, stream, a);
+hipError_t launch_one(const GqaArgs& a, int chunks, hipStream_t stream) {
+  GqaArgs b = a;
+  b.head_chunks = chunks;
+  if ((long long)a.h_kv * chunks > 65535) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((gqa_partial_kernel<E, D, G>), dim3(a.NP, a.h_kv * chunks, a.B), dim3(kThreads), 0, stream, b);
   return hipGetLastError();
 }
 
 template <class E, int D>
 hipError_t launch_d(int G, const GqaArgs& a, hipStream_t s) {
   if constexpr (sizeof(typename E::storage) == 2) {
-    // The position-per-lane kernel reads a paged cache one 32-row tile at a time.
+    // The position-per-lane and matrix-core kernels read a paged cache one
+    // 32-row tile at a time.
     const bool tiles_fit = a.block_table == nullptr || a.page_size % kPoRows == 0;
     if (tiles_fit) {
       switch (G) {
@@ -1120,17 +1031,20 @@ hipError_t launch_d(int G, const GqaArgs& a, hipStream_t s) {
         case 2: return launch_po<D, 2>(a, s);
         case 4: return launch_po<D, 4>(a, s);
         case 8: return launch_po<D, 8>(a, s);
-        default: break;
+        default:
+          if (gqa_matrix(1, D, G)) return launch_gqa_matrix(D, G, a, 0, false, s);
+          break;
       }
     }
   }
   switch (G) {
-    case 1: return launch_one<E, D, 1>(a, s);
-    case 2: return launch_one<E, D, 2>(a, s);
-    case 4: return launch_one<E, D, 4>(a, s);
-    case 8: return launch_one<E, D, 8>(a, s);
-    case 16: return launch_one<E, D, 16>(a, s);
-    default: return hipErrorInvalidValue;
+    case 1: return launch_one<E, D, 1>(a, 1, s);
+    case 2: return launch_one<E, D, 2>(a, 1, s);
+    case 4: return launch_one<E, D, 4>(a, 1, s);
+    case 8: return launch_one<E, D, 8>(a, 1, s);
+    default:  // groups of 16 or more: chunks of 16 heads
+      if (G % 16 != 0) return hipErrorInvalidValue;
+      return launch_one<E, D, 16>(a, G / 16, s);
   }
 }
 
@@ -1160,6 +1074,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const unsigned char* __r
 }  // namespace
 
 int gqa_split_groups(int D, int group) {
+  if (gqa_matrix(1, D, group)) return gqa_matrix_groups(D, group);
   switch (D * 16 + group) {
     case 128 * 16 + 1: return split_groups_dg<128, 1>();
     case 128 * 16 + 2: return split_groups_dg<128, 2>();
@@ -1175,6 +1090,7 @@ int gqa_split_groups(int D, int group) {
 
 hipError_t launch_gqa_split(int D, int group, const GqaArgs& a, int groups, hipStream_t s) {
   if (groups < 1) return hipErrorInvalidValue;
+  if (gqa_matrix(1, D, group)) return launch_gqa_matrix(D, group, a, groups, true, s);
   const dim3 grid((unsigned)groups), block(kThreads);
   switch (D * 16 + group) {
     case 128 * 16 + 1: hipLaunchKernelGGL((gqa_partial_po_kernel<128, 1, true>), grid, block, 0, s, a); break;
@@ -1190,14 +1106,6 @@ hipError_t launch_gqa_split(int D, int group, const GqaArgs& a, int groups, hipS
   return hipGetLastError();
 }
 
-bool gqa_persistent(int dt, int D, int group) {
-  return dt == 1 && (D == 64 || D == 128) && group >= 1 && group <= 8 && (group & (group - 1)) == 0;
-}
-
-bool gqa_supported(int dt, int D, int group) {
-  const bool g_ok = group == 1 || group == 2 || group == 4 || group == 8 || group == 16;
-  return (dt == 0 || dt == 1) && (D == 64 || D == 128) && g_ok;
-}
 
 hipError_t launch_gqa_partial(int dt, int D, int group, const GqaArgs& a, hipStream_t s) {
   if (dt == 1) {

@@ -5,13 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace attn {
+#include "support.h"
 
-// dt: 0 = fp32 storage, 1 = bf16 storage (values of attn_dtype).
-bool gqa_supported(int dt, int D, int group);
-// True when a contiguous-cache decode of this shape runs on the persistent
-// position-per-lane kernel (one work-group per resident slot).
-bool gqa_persistent(int dt, int D, int group);
+namespace attn {
 
 // Arguments of the GQA partial kernels (passed by value as kernel arguments).
 struct GqaArgs {
@@ -31,6 +27,9 @@ struct GqaArgs {
   float qk_scale_log2;        // scale * log2(e)
   float* part_out;            // [B, h_q, NP, D]
   float* part_lse;            // [B, h_q, NP]
+  // Generic kernel only (set by its launcher): the query heads of a group are
+  // taken in head_chunks work-groups of group / head_chunks heads each.
+  int head_chunks;
 };
 
 hipError_t launch_gqa_partial(int dt, int D, int group, const GqaArgs& a, hipStream_t stream);
@@ -44,6 +43,13 @@ hipError_t launch_gqa_partial(int dt, int D, int group, const GqaArgs& a, hipStr
 constexpr int kSplitUnit = 128;
 int gqa_split_groups(int D, int group);  // work-groups of the split launch on the current device
 hipError_t launch_gqa_split(int D, int group, const GqaArgs& a, int groups, hipStream_t stream);
+
+// The matrix-core kernel for bf16 groups of 16 to 128 heads (gqa_matrix.hip):
+// work-groups of a split launch on the current device, and the launch itself
+// (split: the work-balanced split with `groups` work-groups; otherwise fixed
+// partitions of a.P positions, groups <= 0 picks the resident count).
+int gqa_matrix_groups(int D, int group);
+hipError_t launch_gqa_matrix(int D, int group, const GqaArgs& a, int groups, bool split, hipStream_t stream);
 // Merge of the split partials into out [B, h_kv * group, D].
 hipError_t launch_split_merge(int out_dt, const float* part_out, const float* part_lse,
                               const int32_t* seq_lens, int len_add, int window, int B, int h_kv,
@@ -54,16 +60,12 @@ hipError_t launch_kv_append(int dt, const void* k_new, const void* v_new, void* 
                             const int32_t* seq_lens, int B, int h_kv, int D, int T_max,
                             hipStream_t stream);
 
-bool merge_supported(int out_dt, int Dv);
-
 // len_add = 1 for a decode step: each row attends over min(max(seq_lens[b], 0) + 1, T_max)
 // positions instead of min(max(seq_lens[b], 0), T_max). window > 0: only the last
 // `window` of those positions, partitioned from the first of them.
 hipError_t launch_merge(int out_dt, const float* part_out, const float* part_lse,
                         const int32_t* seq_lens, int len_add, int window, int B, int H, int Dv,
                         int T_max, int P, int NP, void* out, hipStream_t stream);
-
-bool mla_supported(int H, int d_c, int d_r);
 
 struct MlaArgs {
   const void* q_nope;         // [B, H, 512]
@@ -97,8 +99,6 @@ hipError_t launch_append_paged(const void* new_a, const void* new_b, void* pages
                                int num_pages, hipStream_t stream);
 
 // MLA absorption products (bf16 in, fp32 accumulation, bf16 out).
-bool absorb_supported(int d_h, int d_c);
-bool up_supported(int d_c, int d_v);
 hipError_t launch_absorb_q(const void* q, const void* w_uk, void* q_lat, int B, int H, int d_h,
                            int d_c, hipStream_t stream);
 hipError_t launch_up_v(const void* o_lat, const void* w_uv, void* out, int B, int H, int d_c,

@@ -334,10 +334,6 @@ hipError_t launch_split_merge(int out_dt, const float* part_out, const float* pa
                             groups, static_cast<uint16_t*>(out), stream);
 }
 
-bool merge_supported(int out_dt, int Dv) {
-  return (out_dt == 0 || out_dt == 1) && Dv >= 4 && Dv % 4 == 0 && Dv <= 1024;
-}
-
 hipError_t launch_merge(int out_dt, const float* part_out, const float* part_lse,
                         const int32_t* seq_lens, int len_add, int window, int B, int H, int Dv,
                         int T_max, int P, int NP, void* out, hipStream_t stream) {

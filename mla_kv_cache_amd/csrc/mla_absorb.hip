@@ -146,8 +146,6 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void up_v_kernel(
 
 }  // namespace
 
-bool absorb_supported(int d_h, int d_c) { return d_h >= 16 && d_h % 16 == 0 && d_c >= 32 && d_c % 32 == 0; }
-bool up_supported(int d_c, int d_v) { return d_c >= 16 && d_c % 16 == 0 && d_v >= 32 && d_v % 32 == 0; }
 
 hipError_t launch_absorb_q(const void* q, const void* w_uk, void* q_lat, int B, int H, int d_h, int d_c,
                            hipStream_t stream) {

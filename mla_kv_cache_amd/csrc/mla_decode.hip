@@ -503,10 +503,6 @@ void mla_partial_kernel(const MlaArgs a) {
 
 }  // namespace
 
-bool mla_supported(int H, int d_c, int d_r) {
-  return d_c == kDc && d_r == kDr && H >= 32 && H % 32 == 0 && (H <= 128 || H % 128 == 0);
-}
-
 
 template <bool PAGED>
 hipError_t launch_mla_nhb(const MlaArgs& a, hipStream_t stream) {

@@ -63,6 +63,16 @@ CASES = [
     (1, 8, 2, 64, 256, torch.float32, [256]),
     (2, 16, 4, 128, 513, torch.float32, [513, 200]),
     (2, 16, 2, 64, 777, torch.float32, [777, 31]),
+    # MQA and groups of 16 to 128 query heads per KV head (matrix-core kernel for bf16,
+    # chunks of 16 heads for fp32)
+    (2, 32, 1, 128, 1000, torch.bfloat16, [1000, 517]),
+    (3, 64, 1, 128, 700, torch.bfloat16, [700, 1, 333]),
+    (2, 128, 1, 128, 600, torch.bfloat16, [600, 45]),
+    (2, 64, 2, 64, 900, torch.bfloat16, [900, 130]),
+    (2, 128, 2, 64, 400, torch.bfloat16, [257, 400]),
+    (2, 32, 2, 128, 800, torch.bfloat16, [800, 799]),
+    (2, 32, 1, 64, 500, torch.float32, [500, 77]),
+    (1, 128, 1, 128, 300, torch.float32, [300]),
 ]
 
 
@@ -97,13 +107,15 @@ def test_tiny_fp32_workload(gpu):
     assert float(np.abs(_f64(out) - ref).max()) <= 1e-5
 
 
-def test_single_position_is_bit_exact(gpu):
+@pytest.mark.parametrize("h_q,h_kv,D", [(16, 4, 128), (32, 1, 128), (128, 1, 128), (64, 2, 64), (32, 2, 128)])
+def test_single_position_is_bit_exact(gpu, h_q, h_kv, D):
     m = _m()
+    g = h_q // h_kv
     for dt in (torch.bfloat16, torch.float32):
-        w = W.small_gqa(3, 16, 4, 128, 300, dtype=dt, seed=5)
+        w = W.small_gqa(3, h_q, h_kv, D, 300, dtype=dt, seed=5)
         (q, k, v, l), (gq, gk, gv, gl) = _inputs(w, gpu, [1, 1, 1])
         out = m.attn_decode_gqa(gq, gk, gv, gl)
-        expect = gv[:, :, 0].repeat_interleave(4, dim=1)
+        expect = gv[:, :, 0].repeat_interleave(g, dim=1)
         assert torch.equal(out, expect)
 
 
@@ -121,9 +133,10 @@ def test_zero_and_clamped_lengths(gpu):
     assert np.all(np.abs(_f64(out) - ref) <= bound)
 
 
-def test_nan_padding_is_never_read(gpu):
+@pytest.mark.parametrize("h_q,h_kv", [(16, 2), (64, 1)])
+def test_nan_padding_is_never_read(gpu, h_q, h_kv):
     m = _m()
-    w = W.small_gqa(2, 16, 2, 128, 1024, seed=7)
+    w = W.small_gqa(2, h_q, h_kv, 128, 1024, seed=7)
     (q, k, v, l), (gq, gk, gv, gl) = _inputs(w, gpu, [700, 129])
     base = m.attn_decode_gqa(gq, gk, gv, gl)
     gk2, gv2 = gk.clone(), gv.clone()
@@ -246,6 +259,8 @@ def test_persistent_split_many_sequences(gpu, B, h_q, h_kv, D):
     (40, 64, 8, 128, 2000, 33),    # ragged, pairs cut between work-groups
     (2, 8, 1, 128, 700, 34),       # MQA
     (5, 16, 8, 64, 130, 35),       # units of one and two tiles' worth
+    (9, 32, 1, 128, 1500, 37),     # MQA on the matrix cores
+    (6, 128, 2, 64, 600, 38),      # groups of 64
 ])
 def test_split_stages_match_one_call(gpu, B, h_q, h_kv, D, T, seed):
     """The work-balanced split: its two stages called one after the other give
@@ -273,9 +288,9 @@ def test_split_stages_match_one_call(gpu, B, h_q, h_kv, D, T, seed):
 
 
 def test_split_stages_reject_unsplit_shapes(gpu):
-    """fp32 and g = 16 run on fixed partitions: the stage entry points say so."""
+    """fp32 caches run on fixed partitions: the stage entry points say so."""
     m = _m()
-    for dt, h_q, h_kv in ((torch.float32, 8, 2), (torch.bfloat16, 16, 1)):
+    for dt, h_q, h_kv in ((torch.float32, 8, 2), (torch.float32, 32, 1)):
         w = W.small_gqa(2, h_q, h_kv, 128, 64, dtype=dt, seed=36)
         _, (gq, gk, gv, gl) = _inputs(w, gpu)
         ws = torch.empty(1 << 20, dtype=torch.uint8, device=gpu)

@@ -67,6 +67,10 @@ CASES = [
     (2, 8, 2, 128, 32, 16, torch.bfloat16, [500, 17]),          # small pages: per-row gather
     (2, 8, 2, 128, 16, 32, torch.bfloat16, [512, 33]),          # one tile per page
     (3, 32, 4, 64, 24, 32, torch.bfloat16, [700, 33, 768]),
+    (3, 32, 1, 128, 16, 64, torch.bfloat16, [1024, 100, 1]),     # MQA, matrix cores
+    (2, 128, 2, 64, 8, 32, torch.bfloat16, [256, 77]),
+    (2, 64, 1, 128, 32, 16, torch.bfloat16, [500, 17]),          # 16-row pages: chunks of 16 heads
+    (2, 32, 1, 64, 10, 32, torch.float32, [300, 12]),
     (2, 16, 4, 128, 8, 64, torch.float32, [512, 200]),
     (2, 16, 8, 64, 20, 16, torch.float32, [320, 100]),
 ]

@@ -39,6 +39,9 @@ CASES = [
     (2, 64, 8, 128, 5000, torch.bfloat16, [5000, 4097], 4096),
     (2, 32, 2, 128, 900, torch.bfloat16, [900, 300], 65),
     (2, 16, 4, 64, 1200, torch.bfloat16, [1200, 10], 513),
+    (3, 32, 1, 128, 2000, torch.bfloat16, [2000, 1000, 40], 300),   # MQA, matrix cores
+    (2, 128, 1, 64, 900, torch.bfloat16, [900, 129], 128),
+    (2, 64, 1, 128, 700, torch.float32, [700, 90], 100),
     (2, 8, 8, 64, 300, torch.float32, [300, 257], 33),
     (2, 16, 4, 128, 513, torch.float32, [513, 200], 256),
 ]

@@ -144,18 +144,17 @@ def test_partials_match_oracle_per_partition(gpu):
         assert float(np.abs(pl[:, :, p] - lse).max()) <= 1e-4
 
 
-def test_full_size_workload_sampled_rows(gpu):
+def test_full_size_workload_every_row(gpu):
     """DeepSeek-V2-shaped layer (B=64, H=128, T=4096) in the benchmark's launch
-    configuration; the oracle checks every head of a sample of sequences."""
+    configuration; the oracle checks every head of every sequence."""
     m = _m()
     w = W.MLA_V2
     (qn, qr, lat, l), (gqn, gqr, glat, gl) = _inputs(w, gpu)
     got = _f64(m.attn_decode_mla(gqn, gqr, glat, gl, w.scale))
     assert np.isfinite(got).all()
     worst = 0.0
-    for b in (0, 17, 40, 63):
+    for b in range(w.B):
         ref = oracle.decode_mla(qn[b:b + 1], qr[b:b + 1], lat[b:b + 1], l[b:b + 1], w.scale, w.d_c)[0]
         worst = max(worst, float(np.abs(got[b] - ref).max()))
-        assert np.all(np.abs(got[b] - ref) <= 2e-3 + _half_ulp_bf16(ref))
-    print(f"mla full size: worst sampled max-abs error {worst:.3e}")
-    assert worst <= 2e-3
+        assert np.all(np.abs(got[b] - ref) <= 2e-3 + _half_ulp_bf16(ref)), b
+    print(f"mla full size: worst max-abs error over all rows {worst:.3e}")

@@ -79,14 +79,21 @@ def test_window_covering_the_sequence_is_the_full_decode(gpu):
         assert torch.equal(out.view(torch.int16), full.view(torch.int16))
 
 
-def test_full_size_window_sampled_rows(gpu):
+def test_full_size_window_every_row(gpu):
     """The 8B-shaped layer (B=32, h_q=32, h_kv=8, D=128, T=4096) with Mistral's 4096 window
-    cut to 1024: sampled rows against the oracle."""
+    cut to 1024, and the 70B-shaped ragged layer with the full 4096 window: every row
+    against the oracle."""
     m = _m()
     wl = W.GQA4_8B
     q, k, v, l = W.gqa_inputs(wl, device="cpu")
     window = 1024
     out = _f64(m.attn_decode_gqa_window(q.to(gpu), k.to(gpu), v.to(gpu), l.to(gpu), window, scale=wl.scale))
-    for b in [0, 13, 31]:
+    for b in range(wl.B):
         ref = oracle.decode_gqa_window(q[b:b + 1], k[b:b + 1], v[b:b + 1], l[b:b + 1], wl.scale, window)[0]
-        assert np.all(np.abs(out[b] - ref) <= 2e-3 + _half_ulp_bf16(ref))
+        assert np.all(np.abs(out[b] - ref) <= 2e-3 + _half_ulp_bf16(ref)), b
+    w8 = W.GQA8_70B
+    q, k, v, l = W.gqa_inputs(w8, device="cpu")
+    out = _f64(m.attn_decode_gqa_window(q.to(gpu), k.to(gpu), v.to(gpu), l.to(gpu), 4096, scale=w8.scale))
+    for b in range(w8.B):
+        ref = oracle.decode_gqa_window(q[b:b + 1], k[b:b + 1], v[b:b + 1], l[b:b + 1], w8.scale, 4096)[0]
+        assert np.all(np.abs(out[b] - ref) <= 2e-3 + _half_ulp_bf16(ref)), b

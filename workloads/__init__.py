@@ -78,10 +78,13 @@ GQA8_70B = GQAWorkload("GQA g=8 70B layer ragged (B=16, h_q=64, h_kv=8, D=128, "
                        "seq_lens~U[1024,32768], T_max=32768, bf16)",
                        B=16, h_q=64, h_kv=8, D=128, T_max=32768, dtype=torch.bfloat16,
                        lens=(1024, 32768))
+MQA_7B = GQAWorkload("MQA 7B-shaped layer (B=32, h_q=32, h_kv=1, D=128, T=32768, bf16)",
+                     B=32, h_q=32, h_kv=1, D=128, T_max=32768, dtype=torch.bfloat16)
 MLA_V2 = MLAWorkload("MLA absorbed DeepSeek-V2 layer (B=64, H=128, d_c=512, d_r=64, T=4096, bf16)",
                      B=64, H=128, d_c=512, d_r=64, T_max=4096)
 
-NAMED = {"tiny": TINY_GQA, "mha7b": MHA_7B, "gqa4": GQA4_8B, "gqa8": GQA8_70B, "mla": MLA_V2}
+NAMED = {"tiny": TINY_GQA, "mha7b": MHA_7B, "gqa4": GQA4_8B, "gqa8": GQA8_70B, "mla": MLA_V2,
+         "mqa": MQA_7B}
 
 
 def _gen(seed: int) -> torch.Generator:

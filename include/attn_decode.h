@@ -169,6 +169,25 @@ int attn_decode_gqa_split_merge(const void* q, const void* k_cache, const void* 
                                 float scale, attn_dtype dt, void* out,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * attn_decode_gqa without a workspace argument. The library supplies the
+ * workspace from one static device array of ATTN_NOALLOC_SCRATCH_BYTES per
+ * device (allocated with the library's code, held until the process ends);
+ * the call itself allocates nothing. Same arguments, checks, kernels and bits
+ * as attn_decode_gqa. Shapes whose workspace
+ * (attn_decode_gqa_workspace_bytes) exceeds ATTN_NOALLOC_SCRATCH_BYTES return
+ * ATTN_ERR_WORKSPACE before anything is launched. Every call on one device
+ * uses the same array: calls that may overlap in time on one device
+ * (different streams, or host threads without ordering) race and give
+ * undefined results; calls ordered on one stream are safe. Nothing in the
+ * array needs to be zero on entry. ATTN_ERR_HIP if the array's device address
+ * cannot be obtained. */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int attn_decode_gqa_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, int B, int h_q, int h_kv, int D, int T_max,
+                            float scale, attn_dtype dt, void* out, hipStream_t stream);
+
 /* Sliding-window decode ("Grouped-Query Attention: Fewer KV Heads, Same
  * Quality", section "GQA and Related KV-Head Choices in Modern Architectures":
  * Mistral 7B pairs grouped KV heads with a window of w = 4096 positions). Each

@@ -34,6 +34,8 @@ SIGNATURES = {
     "attn_decode_gqa_workspace_bytes": (_c_size, [_c_int] * 6),
     "attn_decode_gqa": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _c_float, _c_int, _vp, _vp, _c_size, _vp]),
+    "attn_decode_gqa_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                         _c_float, _c_int, _vp, _vp]),
     "attn_decode_gqa_split": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_float, _c_int, _vp, _vp, _c_size, _vp]),
     "attn_decode_gqa_split_merge": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,

@@ -22,7 +22,7 @@ LIB_NAME = "libattn_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["attn_decode.cpp", "gqa_decode.hip", "gqa_matrix.hip", "lse_merge.hip", "mla_decode.hip",
-           "mla_absorb.hip"]
+           "mla_absorb.hip", "noalloc.hip"]
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are switched off for all device code.

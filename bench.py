@@ -14,8 +14,10 @@ stream (``config.breakdown``); the timed pass of K steps records events only
 around the dominant partial kernel (``roofline``), because every event record
 adds a few microseconds to a step. ``value`` = KV-cache bytes of the step
 (valid positions only) divided by the wall time of a step in the timed pass.
-The MHA (Llama-2-7B layer) workload is timed separately and reported in
-``config.breakdown`` only.
+The MHA (Llama-2-7B layer) and MQA (7B-shaped, one KV head) workloads are
+timed separately, and the tiny fp32 workload as the latency of one call; they
+are reported in ``config.breakdown`` only. Per-call and per-step figures come
+with their median and 10th/90th percentiles over the K steps.
 
 Inputs are seeded synthetic tensors (``workloads``), resident in HBM before
 the timed region. The working set (> 1.6 GB per step) is far larger than the
@@ -44,6 +46,27 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def pct(xs, q):
+    """q-th percentile (0..100) of a list, linear interpolation between order statistics."""
+    ys = sorted(xs)
+    if not ys:
+        return float("nan")
+    k = (len(ys) - 1) * q / 100.0
+    lo = int(math.floor(k))
+    hi = min(lo + 1, len(ys) - 1)
+    return ys[lo] + (ys[hi] - ys[lo]) * (k - lo)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ----------------------------------------------------------------------------- algorithmic work
@@ -276,35 +299,48 @@ def time_next_rows(m, W, dev, stream, items, warmup, iters):
 # ----------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(items, budget_s=15.0):
-    """Time the fp64 oracle on whole sequences of each workload until the budget is spent."""
+    """Time the fp64 oracle on whole sequences of each workload until the budget is spent.
+
+    Reported: KV GB/s of the oracle (sampled bytes / time), the host's CPU model
+    and thread count, and the oracle's decode steps/s, estimated as one over the
+    sum, across workloads, of the sampled time scaled up to the whole workload
+    (by its share of the workload's KV bytes)."""
     import numpy as np  # noqa: F401
     import torch
     import oracle
     cores = len(os.sched_getaffinity(0))
     torch.set_num_threads(cores)
     done_bytes, t_used, parts = 0, 0.0, []
+    step_est = 0.0
     per = budget_s / max(1, len(items))
     for name, kind, w, cpu in items:
         t0 = time.perf_counter()
         nseq = 0
+        wl_bytes = 0
+        total = gqa_work(w, cpu[3].tolist())[0] if kind == "gqa" else mla_work(w, cpu[3].tolist())[0]
         for b in range(w.B):
             if kind == "gqa":
                 q, k, v, lens = cpu
                 oracle.decode_gqa(q[b:b + 1], k[b:b + 1], v[b:b + 1], lens[b:b + 1], w.scale)
-                done_bytes += gqa_work(w, lens[b:b + 1])[0]
+                wl_bytes += gqa_work(w, lens[b:b + 1])[0]
             else:
                 qn, qr, lat, lens = cpu
                 oracle.decode_mla(qn[b:b + 1], qr[b:b + 1], lat[b:b + 1], lens[b:b + 1], w.scale, w.d_c)
-                done_bytes += mla_work(w, lens[b:b + 1])[0]
+                wl_bytes += mla_work(w, lens[b:b + 1])[0]
             nseq += 1
             if time.perf_counter() - t0 >= per:
                 break
         dt = time.perf_counter() - t0
         t_used += dt
+        done_bytes += wl_bytes
+        step_est += dt * total / max(1, wl_bytes)
         parts.append(f"{name}: {nseq}/{w.B} sequences in {dt:.1f}s")
     return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle", "sample": "; ".join(parts) +
-            " (fp64 oracle, whole sequences, KV bytes of the sampled sequences / time)"}
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "decode_steps_per_s": round(1.0 / step_est, 4) if step_est > 0 else None,
+            "sample": "; ".join(parts) +
+            " (fp64 oracle, whole sequences, KV bytes of the sampled sequences / time; "
+            "steps/s scales each workload's sampled time to all its sequences)"}
 
 
 # ----------------------------------------------------------------------------- main
@@ -316,7 +352,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
-    ap.add_argument("--skip-mha", action="store_true", help="do not time the MHA breakdown workload")
+    ap.add_argument("--skip-mha", action="store_true", help="do not time the MHA and MQA breakdown workloads")
     ap.add_argument("--skip-next", action="store_true",
                     help="do not time the decode-step and sliding-window variants")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -354,13 +390,14 @@ def main():
         mla_ok = False
 
     # ---- inputs (seeded, drawn on the host, copied once into HBM)
-    specs = [("gqa4", "gqa", W.GQA4_8B), ("gqa8", "gqa", W.GQA8_70B)]
+    specs = [("gqa4", "gqa", W.GQA4_8B, True), ("gqa8", "gqa", W.GQA8_70B, True)]
     if mla_ok:
-        specs.append(("mla", "mla", W.MLA_V2))
+        specs.append(("mla", "mla", W.MLA_V2, True))
     if not args.skip_mha:
-        specs.append(("mha7b", "gqa", W.MHA_7B))
+        specs.append(("mha7b", "gqa", W.MHA_7B, False))
+        specs.append(("mqa", "gqa", W.MQA_7B, False))
     items, cpu_items = [], []
-    for name, kind, w in specs:
+    for name, kind, w, in_step in specs:
         t0 = time.perf_counter()
         cpu = W.gqa_inputs(w) if kind == "gqa" else W.mla_inputs(w)
         gpu = tuple(x.to(dev) for x in cpu)
@@ -371,29 +408,19 @@ def main():
             P, NP, ws = m.attn_decode_gqa_plan(w.B, w.h_q, w.h_kv, w.D, w.T_max, w.dtype)
             out = torch.empty_like(q)
             kv, other, flops = gqa_work(w, lens)
-            if w.dtype == torch.bfloat16 and w.group <= 8:
-                # attn_decode_gqa's work-balanced split, one stage per call
-                wsb = torch.empty(ws, dtype=torch.uint8, device=dev)
-                P, NP = "work-balanced split, 128-position units", None
+            # attn_decode_gqa's work-balanced split (bf16), one stage per call
+            wsb = torch.empty(ws, dtype=torch.uint8, device=dev)
+            P, NP = "work-balanced split, 128-position units", None
 
-                def partial(q=q, k=k, v=v, gl=gl, wsb=wsb, out=out, w=w):
-                    m.attn_decode_gqa_split(q, k, v, gl, wsb, scale=w.scale, out=out)
+            def partial(q=q, k=k, v=v, gl=gl, wsb=wsb, out=out, w=w):
+                m.attn_decode_gqa_split(q, k, v, gl, wsb, scale=w.scale, out=out)
 
-                def merge(q=q, k=k, v=v, gl=gl, wsb=wsb, out=out, w=w):
-                    m.attn_decode_gqa_split_merge(q, k, v, gl, wsb, scale=w.scale, out=out)
-                kname = f"gqa_partial_po_kernel<{w.D}, {w.group}, true>"
-            else:
-                po = torch.empty((w.B, w.h_q, NP, w.D), dtype=torch.float32, device=dev)
-                pl = torch.empty((w.B, w.h_q, NP), dtype=torch.float32, device=dev)
-
-                def partial(q=q, k=k, v=v, gl=gl, P=P, po=po, pl=pl, w=w):
-                    m.attn_decode_gqa_partial(q, k, v, gl, P, scale=w.scale, part_out=po, part_lse=pl)
-
-                def merge(po=po, pl=pl, gl=gl, P=P, out=out, w=w):
-                    m.attn_decode_merge(po, pl, gl, w.T_max, P, out=out)
-                kname = (f"gqa_partial_po_kernel<{w.D}, {w.group}, false>" if w.group <= 8
-                         else f"gqa_partial_kernel<BF16Elem, {w.D}, {w.group}>")
-            src = os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "gqa_decode.hip")
+            def merge(q=q, k=k, v=v, gl=gl, wsb=wsb, out=out, w=w):
+                m.attn_decode_gqa_split_merge(q, k, v, gl, wsb, scale=w.scale, out=out)
+            kname = (f"gqa_partial_po_kernel<{w.D}, {w.group}, true>" if w.group <= 8
+                     else f"gqa_matrix_kernel<{w.D}, {w.group}, true>")
+            src = os.path.join(ROOT, "mla_kv_cache_amd", "csrc",
+                               "gqa_decode.hip" if w.group <= 8 else "gqa_matrix.hip")
         else:
             qn, qr, lat, gl = gpu
             P, NP, ws = m.attn_decode_mla_plan(w.B, w.H, w.d_c, w.d_r, w.T_max)
@@ -411,8 +438,8 @@ def main():
             src = os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "mla_decode.hip")
         items.append(dict(name=name, kind=kind, w=w, partial=partial, merge=merge, kv=kv,
                           other=other, flops=flops, P=P, NP=NP, kname=kname, src=src,
-                          in_step=name != "mha7b", gpu=gpu))
-        if name != "mha7b":
+                          in_step=in_step, gpu=gpu))
+        if in_step:
             cpu_items.append((name, kind, w, cpu))
         else:
             del cpu
@@ -420,9 +447,12 @@ def main():
 
     step_items = [it for it in items if it["in_step"]]
 
-    def run_step(record=None, only=None, only_evs=None):
+    def run_step(record=None, only=None, only_evs=None, step_evs=None):
         # record: events around every kernel; only: the name of the one
-        # workload whose partial kernel alone is bracketed by only_evs.
+        # workload whose partial kernel alone is bracketed by only_evs;
+        # step_evs: one event at the start of the step.
+        if step_evs is not None:
+            step_evs.record(stream)
         for it in step_items:
             if record is not None:
                 record[it["name"]][0].record(stream)
@@ -437,37 +467,58 @@ def main():
             if record is not None:
                 record[it["name"]][2].record(stream)
 
+    def summary_us(ms_list):
+        us = [x * 1e3 for x in ms_list]
+        return {"median": round(pct(us, 50), 2), "p10": round(pct(us, 10), 2),
+                "p90": round(pct(us, 90), 2), "mean": round(sum(us) / len(us), 2)}
+
+    def breakdown_entry(it, pt, mt, note=None):
+        ct = [a + b for a, b in zip(pt, mt)]
+        call_ms, part_ms, merge_ms = pct(ct, 50), pct(pt, 50), pct(mt, 50)
+        it["partial_ms"] = part_ms
+        e = {"workload": it["w"].name, "partition_size": it["P"], "partitions": it["NP"],
+             "call_us": summary_us(ct), "partial_us": round(part_ms * 1e3, 2),
+             "merge_us": round(merge_ms * 1e3, 2), "kv_bytes": it["kv"],
+             "kv_GBps": round(it["kv"] / (call_ms * 1e-3) / 1e9, 1),
+             "kv_frac_hbm_peak": round(it["kv"] / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+             "partial_kernel_GBps": round((it["kv"] + it["other"]) / (part_ms * 1e-3) / 1e9, 1),
+             "partial_frac_hbm_peak": round((it["kv"] + it["other"]) / (part_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if it["kind"] == "mla":
+            tf = it["flops"] / (call_ms * 1e-3) / 1e12
+            e["call_TFLOPs"] = round(tf, 1)
+            e["mfma_frac_bf16_peak"] = round(tf / BF16_MFMA_PEAK_TFLOPS, 4)
+        if note:
+            e["note"] = note
+        return e
+
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
 
     # Per-kernel breakdown: a pass of its own with events around every
     # kernel (each event record adds a few microseconds to the step, so this
-    # pass is not the one whose wall time is reported).
+    # pass is not the one whose wall time is reported). Medians and p10/p90
+    # are over the K steps; kv_frac_hbm_peak is the whole call's (partial
+    # kernel + merge) median.
     evs = [{it["name"]: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for it in step_items}
            for _ in range(args.steps)]
-    for s in range(args.steps):
-        run_step(evs[s])
+    for s_ in range(args.steps):
+        run_step(evs[s_])
     torch.cuda.synchronize()
 
     breakdown = {}
     for it in step_items:
-        pt = [evs[s][it["name"]][0].elapsed_time(evs[s][it["name"]][1]) for s in range(args.steps)]
-        mt = [evs[s][it["name"]][1].elapsed_time(evs[s][it["name"]][2]) for s in range(args.steps)]
-        it["partial_ms"] = sum(pt) / len(pt)
-        it["merge_ms"] = sum(mt) / len(mt)
-        tot = it["partial_ms"] + it["merge_ms"]
-        breakdown[it["name"]] = {
-            "workload": it["w"].name, "partition_size": it["P"], "partitions": it["NP"],
-            "partial_us": round(it["partial_ms"] * 1e3, 2), "merge_us": round(it["merge_ms"] * 1e3, 2),
-            "kv_bytes": it["kv"], "kv_GBps": round(it["kv"] / (tot * 1e-3) / 1e9, 1),
-            "kv_frac_hbm_peak": round(it["kv"] / (tot * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "partial_kernel_GBps": round((it["kv"] + it["other"]) / (it["partial_ms"] * 1e-3) / 1e9, 1),
-        }
-        if it["kind"] == "mla":
-            tf = it["flops"] / (it["partial_ms"] * 1e-3) / 1e12
-            breakdown[it["name"]]["partial_TFLOPs"] = round(tf, 1)
-            breakdown[it["name"]]["mfma_frac_bf16_peak"] = round(tf / BF16_MFMA_PEAK_TFLOPS, 4)
+        pt = [evs[s_][it["name"]][0].elapsed_time(evs[s_][it["name"]][1]) for s_ in range(args.steps)]
+        mt = [evs[s_][it["name"]][1].elapsed_time(evs[s_][it["name"]][2]) for s_ in range(args.steps)]
+        breakdown[it["name"]] = breakdown_entry(it, pt, mt)
+
+    # Step-time distribution: one event at each step boundary.
+    sevs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    for s_ in range(args.steps):
+        run_step(step_evs=sevs[s_])
+    sevs[-1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = [sevs[i].elapsed_time(sevs[i + 1]) for i in range(args.steps)]
 
     # The timed region: K steps with events only around the dominant partial
     # kernel (the roofline's launch duration comes from these).
@@ -477,14 +528,14 @@ def main():
         run_step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        run_step(only=dom["name"], only_evs=dom_evs[s])
+    for s_ in range(args.steps):
+        run_step(only=dom["name"], only_evs=dom_evs[s_])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     dom_ms = sum(e[0].elapsed_time(e[1]) for e in dom_evs) / args.steps
 
-    # MHA breakdown: timed on its own, not part of the step.
+    # Workloads timed on their own, not part of the step (MHA 7B, MQA).
     for it in items:
         if it["in_step"]:
             continue
@@ -502,14 +553,26 @@ def main():
             torch.cuda.synchronize()
             pts.append(e[0].elapsed_time(e[1]))
             mts.append(e[1].elapsed_time(e[2]))
-        p_ms, m_ms = sum(pts) / len(pts), sum(mts) / len(mts)
-        breakdown[it["name"]] = {
-            "workload": it["w"].name, "partition_size": it["P"], "partitions": it["NP"],
-            "partial_us": round(p_ms * 1e3, 2), "merge_us": round(m_ms * 1e3, 2),
-            "kv_bytes": it["kv"], "kv_GBps": round(it["kv"] / ((p_ms + m_ms) * 1e-3) / 1e9, 1),
-            "kv_frac_hbm_peak": round(it["kv"] / ((p_ms + m_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "note": "timed alone, not part of the step",
-        }
+        breakdown[it["name"]] = breakdown_entry(it, pts, mts, note="timed alone, not part of the step")
+
+    # The tiny fp32 workload: latency of one library call (latency-bound, microseconds only).
+    tw = W.TINY_GQA
+    tq, tk, tv, tl = (x.to(dev) for x in W.gqa_inputs(tw))
+    tws = torch.empty(m.attn_decode_gqa_workspace_bytes(tw.B, tw.h_q, tw.h_kv, tw.D, tw.T_max, tw.dtype),
+                      dtype=torch.uint8, device=dev)
+    tout = torch.empty_like(tq)
+    for _ in range(max(1, args.warmup)):
+        m.attn_decode_gqa(tq, tk, tv, tl, scale=tw.scale, out=tout, workspace=tws)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    tts = []
+    for _ in range(args.steps):
+        e[0].record(stream)
+        m.attn_decode_gqa(tq, tk, tv, tl, scale=tw.scale, out=tout, workspace=tws)
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        tts.append(e[0].elapsed_time(e[1]))
+    breakdown["tiny"] = {"workload": tw.name, "call_us": summary_us(tts),
+                         "note": "latency-bound (262 KB of KV): microseconds only, no roofline fraction"}
 
     if not args.skip_next:
         breakdown["next_rows"] = time_next_rows(m, W, dev, stream, items, args.warmup, args.steps)
@@ -523,7 +586,9 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": dom["kname"], "workload": dom["w"].name,
                 "avg_launch_us": round(dom_ms * 1e3, 2),
-                "algorithmic_bytes_per_launch": dom["kv"] + dom["other"]}
+                "algorithmic_bytes_per_launch": dom["kv"] + dom["other"],
+                "whole_call_frac": {it["name"]: breakdown[it["name"]]["kv_frac_hbm_peak"]
+                                    for it in items}}
 
     res = {
         "metric": "KV-cache GB/s per decode step (GQA g=4, GQA g=8, MLA)",
@@ -534,6 +599,7 @@ def main():
                    "step_kv_bytes": step_kv,
                    "kv_frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
                    "decode_steps_per_s": round(1e3 / ms_per_step, 2),
+                   "step_us": summary_us(step_ms),
                    "breakdown": breakdown},
         "roofline": roofline,
     }

@@ -23,7 +23,7 @@ __all__ = [
     "AttnError", "load",
     "attn_kv_cache_bytes", "attn_mla_cache_bytes",
     "attn_decode_gqa_plan", "attn_decode_gqa_workspace_bytes", "attn_decode_gqa",
-    "attn_decode_gqa_split", "attn_decode_gqa_split_merge",
+    "attn_decode_gqa_noalloc", "attn_decode_gqa_split", "attn_decode_gqa_split_merge",
     "attn_decode_gqa_partial", "attn_decode_merge",
     "attn_decode_mla_plan", "attn_decode_mla_workspace_bytes", "attn_decode_mla",
     "attn_decode_mla_partial",
@@ -150,6 +150,24 @@ def attn_decode_gqa(q, k_cache, v_cache, seq_lens, scale: Optional[float] = None
                                   h_kv, D, T_max, scale, dt, _ptr(out), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(dev)),
            "attn_decode_gqa")
+    return out
+
+
+def attn_decode_gqa_noalloc(q, k_cache, v_cache, seq_lens, scale: Optional[float] = None,
+                            out: Optional[torch.Tensor] = None):
+    """attn_decode_gqa with the library's static device scratch as the workspace (no
+    allocation in the call; only `out` is allocated here when the caller passes none)."""
+    B, h_q, h_kv, D, T_max = _gqa_shapes(q, k_cache, v_cache)
+    dev = _dev(q, k_cache, v_cache, seq_lens)
+    _lens(seq_lens, B)
+    dt = _dt(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out)
+    _check(load().attn_decode_gqa_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B, h_q,
+                                          h_kv, D, T_max, scale, dt, _ptr(out), _stream(dev)),
+           "attn_decode_gqa_noalloc")
     return out
 
 

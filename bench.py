@@ -472,8 +472,7 @@ def main():
         return {"median": round(pct(us, 50), 2), "p10": round(pct(us, 10), 2),
                 "p90": round(pct(us, 90), 2), "mean": round(sum(us) / len(us), 2)}
 
-    def breakdown_entry(it, pt, mt, note=None):
-        ct = [a + b for a, b in zip(pt, mt)]
+    def breakdown_entry(it, pt, mt, ct, note=None):
         call_ms, part_ms, merge_ms = pct(ct, 50), pct(pt, 50), pct(mt, 50)
         it["partial_ms"] = part_ms
         e = {"workload": it["w"].name, "partition_size": it["P"], "partitions": it["NP"],
@@ -506,11 +505,24 @@ def main():
         run_step(evs[s_])
     torch.cuda.synchronize()
 
+    # Whole calls: a pass with events only around each call (partial kernel +
+    # merge, as one library call issues them), no event between the two.
+    cevs = [{it["name"]: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for it in step_items}
+            for _ in range(args.steps)]
+    for s_ in range(args.steps):
+        for it in step_items:
+            cevs[s_][it["name"]][0].record(stream)
+            it["partial"]()
+            it["merge"]()
+            cevs[s_][it["name"]][1].record(stream)
+    torch.cuda.synchronize()
+
     breakdown = {}
     for it in step_items:
         pt = [evs[s_][it["name"]][0].elapsed_time(evs[s_][it["name"]][1]) for s_ in range(args.steps)]
         mt = [evs[s_][it["name"]][1].elapsed_time(evs[s_][it["name"]][2]) for s_ in range(args.steps)]
-        breakdown[it["name"]] = breakdown_entry(it, pt, mt)
+        ct = [cevs[s_][it["name"]][0].elapsed_time(cevs[s_][it["name"]][1]) for s_ in range(args.steps)]
+        breakdown[it["name"]] = breakdown_entry(it, pt, mt, ct)
 
     # Step-time distribution: one event at each step boundary.
     sevs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -535,25 +547,33 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     dom_ms = sum(e[0].elapsed_time(e[1]) for e in dom_evs) / args.steps
 
-    # Workloads timed on their own, not part of the step (MHA 7B, MQA).
+    # Workloads timed on their own, not part of the step (MHA 7B, MQA): calls
+    # back to back on the stream, one pass with events around each kernel and
+    # one with events around each whole call.
     for it in items:
         if it["in_step"]:
             continue
         for _ in range(args.warmup):
             it["partial"]()
             it["merge"]()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        pts, mts = [], []
-        for _ in range(args.steps):
-            e[0].record(stream)
+        e3 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        e2 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for s_ in range(args.steps):
+            e3[s_][0].record(stream)
             it["partial"]()
-            e[1].record(stream)
+            e3[s_][1].record(stream)
             it["merge"]()
-            e[2].record(stream)
-            torch.cuda.synchronize()
-            pts.append(e[0].elapsed_time(e[1]))
-            mts.append(e[1].elapsed_time(e[2]))
-        breakdown[it["name"]] = breakdown_entry(it, pts, mts, note="timed alone, not part of the step")
+            e3[s_][2].record(stream)
+        for s_ in range(args.steps):
+            e2[s_][0].record(stream)
+            it["partial"]()
+            it["merge"]()
+            e2[s_][1].record(stream)
+        torch.cuda.synchronize()
+        pts = [e[0].elapsed_time(e[1]) for e in e3]
+        mts = [e[1].elapsed_time(e[2]) for e in e3]
+        cts = [e[0].elapsed_time(e[1]) for e in e2]
+        breakdown[it["name"]] = breakdown_entry(it, pts, mts, cts, note="timed alone, not part of the step")
 
     # The tiny fp32 workload: latency of one library call (latency-bound, microseconds only).
     tw = W.TINY_GQA
@@ -563,16 +583,16 @@ def main():
     tout = torch.empty_like(tq)
     for _ in range(max(1, args.warmup)):
         m.attn_decode_gqa(tq, tk, tv, tl, scale=tw.scale, out=tout, workspace=tws)
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    tts = []
-    for _ in range(args.steps):
-        e[0].record(stream)
+    te = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for s_ in range(args.steps):
+        te[s_][0].record(stream)
         m.attn_decode_gqa(tq, tk, tv, tl, scale=tw.scale, out=tout, workspace=tws)
-        e[1].record(stream)
-        torch.cuda.synchronize()
-        tts.append(e[0].elapsed_time(e[1]))
+        te[s_][1].record(stream)
+    torch.cuda.synchronize()
+    tts = [e[0].elapsed_time(e[1]) for e in te]
     breakdown["tiny"] = {"workload": tw.name, "call_us": summary_us(tts),
-                         "note": "latency-bound (262 KB of KV): microseconds only, no roofline fraction"}
+                         "note": "latency-bound (262 KB of KV): microseconds only, no roofline fraction; "
+                                 "calls back to back on the stream"}
 
     if not args.skip_next:
         breakdown["next_rows"] = time_next_rows(m, W, dev, stream, items, args.warmup, args.steps)

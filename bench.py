@@ -155,8 +155,10 @@ def write_traffic(fetch_csv: str, write_csv: str, command: str):
     attention kernel; each moves COPY_CAL_BYTES in and out, so
     factor = COPY_CAL_BYTES / (counter KiB * 1024) converts a counter reading to bytes."""
     srcs = {"gqa_partial": os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "gqa_decode.hip"),
+            "gqa_matrix": os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "gqa_matrix.hip"),
             "mla_partial": os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "mla_decode.hip"),
-            "lse_merge": os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "lse_merge.hip")}
+            "lse_merge": os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "lse_merge.hip"),
+            "split_merge": os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "lse_merge.hip")}
     res = {"command": command, "copy_bytes": COPY_CAL_BYTES, "kernels": {}}
     per = {}
     for cname, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -185,6 +187,67 @@ def write_traffic(fetch_csv: str, write_csv: str, command: str):
         json.dump(res, f, indent=1)
         f.write("\n")
     print(json.dumps(res, indent=1))
+
+
+def summarize_counters(csvs, trace_csv=None):
+    """Markdown table of per-dispatch hardware counters averaged per kernel, from
+    rocprofv3 --pmc counter_collection CSVs (one or more passes).
+
+    Derived columns (MI355X: 8 XCDs, 256 CUs, 1,024 SIMDs):
+      cycles per dispatch = GRBM_GUI_ACTIVE / 8 (the counter sums the 8 XCDs);
+      MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1,024 SIMDs x cycles);
+      VALU busy = 4 x SQ_ACTIVE_INST_VALU / (1,024 x cycles) (quad-cycles of VALU issue, per SIMD);
+      LDS bank-conflict share = SQ_LDS_BANK_CONFLICT / (4 x SQ_ACTIVE_INST_LDS);
+      L2 hit rate = TCC_HIT / (TCC_HIT + TCC_MISS)."""
+    import csv
+    per = {}
+    for path in csvs:
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                name = _norm_kernel_name(row["Kernel_Name"])
+                if name.startswith("__amd"):
+                    continue
+                d = per.setdefault(name, {})
+                d.setdefault(row["Counter_Name"], {}).setdefault(row["Dispatch_Id"], 0.0)
+                d[row["Counter_Name"]][row["Dispatch_Id"]] += float(row["Counter_Value"])
+    dur = {}
+    if trace_csv:
+        with open(trace_csv, newline="") as f:
+            for row in csv.DictReader(f):
+                name = _norm_kernel_name(row["Kernel_Name"])
+                dur.setdefault(name, []).append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+
+    def avg(d, c):
+        v = d.get(c)
+        return sum(v.values()) / len(v) if v else None
+
+    lines = ["| Kernel | dispatches | us (trace) | cycles / dispatch | MHz | MFMA busy | VALU busy | "
+             "LDS bank-conflict share | L2 hit rate |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for name, d in sorted(per.items()):
+        gui = avg(d, "GRBM_GUI_ACTIVE")
+        cyc = gui / 8 if gui else None
+        us = sum(dur[name]) / len(dur[name]) if name in dur else None
+        mfma, valu = avg(d, "SQ_VALU_MFMA_BUSY_CYCLES"), avg(d, "SQ_ACTIVE_INST_VALU")
+        bank, lds = avg(d, "SQ_LDS_BANK_CONFLICT"), avg(d, "SQ_ACTIVE_INST_LDS")
+        hit, miss = avg(d, "TCC_HIT"), avg(d, "TCC_MISS")
+        ndisp = max(len(v) for v in d.values())
+        f = lambda x, fmt: (fmt.format(x) if x is not None else "-")
+        lines.append("| `{}` | {} | {} | {} | {} | {} | {} | {} | {} |".format(
+            name, ndisp, f(us, "{:.1f}"), f(cyc, "{:,.0f}"),
+            f(cyc / us if cyc and us else None, "{:,.0f}"),
+            f(mfma / (1024 * cyc) if mfma is not None and cyc else None, "{:.1%}"),
+            f(4 * valu / (1024 * cyc) if valu is not None and cyc else None, "{:.1%}"),
+            f(bank / (4 * lds) if bank is not None and lds else None, "{:.2%}"),
+            f(hit / (hit + miss) if hit is not None and miss is not None and hit + miss > 0 else None, "{:.1%}")))
+    raw = ["", "Raw averages per dispatch:", "",
+           "| Kernel | " + " | ".join(sorted({c for d in per.values() for c in d})) + " |",
+           "|---|" + "---|" * len({c for d in per.values() for c in d})]
+    cols = sorted({c for d in per.values() for c in d})
+    for name, d in sorted(per.items()):
+        raw.append("| `{}` | ".format(name) + " | ".join(
+            "{:,.0f}".format(avg(d, c)) if avg(d, c) is not None else "-" for c in cols) + " |")
+    return "\n".join(lines + raw)
 
 
 # ----------------------------------------------------------------------------- widened rows
@@ -360,7 +423,14 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two rocprofv3 counter CSVs and exit")
     ap.add_argument("--traffic-command", default="", help="command recorded with --traffic-from")
+    ap.add_argument("--counters-from", nargs="+", metavar="CSV",
+                    help="print a per-kernel table of rocprofv3 counter CSVs (and exit)")
+    ap.add_argument("--trace", metavar="KERNEL_TRACE_CSV", help="kernel trace for --counters-from durations")
     args = ap.parse_args()
+
+    if args.counters_from:
+        print(summarize_counters(args.counters_from, args.trace))
+        return
 
     if args.traffic_from:
         write_traffic(args.traffic_from[0], args.traffic_from[1], args.traffic_command)

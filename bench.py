@@ -156,6 +156,7 @@ def write_traffic(fetch_csv: str, write_csv: str, command: str):
     factor = COPY_CAL_BYTES / (counter KiB * 1024) converts a counter reading to bytes."""
     srcs = {"gqa_partial": os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "gqa_decode.hip"),
             "gqa_matrix": os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "gqa_matrix.hip"),
+            "gqa_mma16": os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "gqa_mma16.hip"),
             "mla_partial": os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "mla_decode.hip"),
             "lse_merge": os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "lse_merge.hip"),
             "split_merge": os.path.join(ROOT, "mla_kv_cache_amd", "csrc", "lse_merge.hip")}
@@ -487,10 +488,13 @@ def main():
 
             def merge(q=q, k=k, v=v, gl=gl, wsb=wsb, out=out, w=w):
                 m.attn_decode_gqa_split_merge(q, k, v, gl, wsb, scale=w.scale, out=out)
-            kname = (f"gqa_partial_po_kernel<{w.D}, {w.group}, true>" if w.group <= 8
-                     else f"gqa_matrix_kernel<{w.D}, {w.group}, true>")
-            src = os.path.join(ROOT, "mla_kv_cache_amd", "csrc",
-                               "gqa_decode.hip" if w.group <= 8 else "gqa_matrix.hip")
+            if w.group <= 4:
+                kname, srcf = f"gqa_partial_po_kernel<{w.D}, {w.group}, true>", "gqa_decode.hip"
+            elif w.group <= 64:
+                kname, srcf = f"gqa_mma16_kernel<{w.D}, {w.group}, true>", "gqa_mma16.hip"
+            else:
+                kname, srcf = f"gqa_matrix_kernel<{w.D}, {w.group}, true>", "gqa_matrix.hip"
+            src = os.path.join(ROOT, "mla_kv_cache_amd", "csrc", srcf)
         else:
             qn, qr, lat, gl = gpu
             P, NP, ws = m.attn_decode_mla_plan(w.B, w.H, w.d_c, w.d_r, w.T_max)

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libattn_decode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["attn_decode.cpp", "gqa_decode.hip", "gqa_matrix.hip", "lse_merge.hip", "mla_decode.hip",
+SOURCES = ["attn_decode.cpp", "gqa_decode.hip", "gqa_matrix.hip", "gqa_mma16.hip", "lse_merge.hip", "mla_decode.hip",
            "mla_absorb.hip", "noalloc.hip"]
 
 ARCH = "gfx950"

@@ -73,8 +73,7 @@ int check_gqa_shape(const GqaShape& s) {
 // kernel aims for about 8192 work-groups (32 per CU).
 int gqa_auto_partition(const GqaShape& s) {
   const int64_t pairs = int64_t(s.B) * s.h_kv;
-  const int G = s.h_q / s.h_kv;
-  const int64_t target = attn::gqa_persistent(int(s.dt), s.D, G) || attn::gqa_matrix(int(s.dt), s.D, G) ? 2048 : 8192;
+  const int64_t target = s.dt == ATTN_BF16 ? 2048 : 8192;
   const int64_t want = (int64_t(s.T_max) * pairs + target - 1) / target;
   int P = 512;
   while (P < want && P < 4096) P <<= 1;
@@ -85,12 +84,15 @@ size_t partial_bytes(int64_t rows, int NP, int Dv) {
   return align_up(size_t(rows) * NP * Dv * sizeof(float)) + align_up(size_t(rows) * NP * sizeof(float));
 }
 
-// Split decode: work-groups of the launch (0: the shape does not take it) and
-// its workspace, one partial per slot (work-groups + B * h_kv slots of G heads).
-int gqa_split_groups(const GqaShape& s) {
-  const int G = s.h_q / s.h_kv;
-  return attn::gqa_persistent(int(s.dt), s.D, G) || attn::gqa_matrix(int(s.dt), s.D, G)
-             ? attn::gqa_split_groups(s.D, G) : 0;
+// Split decode (bf16): work-groups of the launch for a page size (0:
+// contiguous cache; 0 groups: the shape runs on fixed partitions), and the
+// most any page size can use, which the plan's workspace covers. Workspace:
+// one partial per slot (work-groups + B * h_kv slots of G heads).
+int gqa_split_groups(const GqaShape& s, int page_size) {
+  return s.dt == ATTN_BF16 ? attn::gqa_split_groups(s.D, s.h_q / s.h_kv, page_size) : 0;
+}
+int gqa_split_groups_max(const GqaShape& s) {
+  return s.dt == ATTN_BF16 ? attn::gqa_split_groups_max(s.D, s.h_q / s.h_kv) : 0;
 }
 size_t split_bytes(const GqaShape& s, int groups) {
   return partial_bytes((int64_t(groups) + int64_t(s.B) * s.h_kv) * (s.h_q / s.h_kv), 1, s.D);
@@ -238,7 +240,7 @@ int attn_decode_gqa_plan(int B, int h_q, int h_kv, int D, int T_max, attn_dtype 
   if (st != ATTN_OK) return st;
   const int P = gqa_auto_partition(s);
   const int NP = ceil_div(T_max, P);
-  const int groups = gqa_split_groups(s);
+  const int groups = gqa_split_groups_max(s);
   size_t ws = partial_bytes(int64_t(B) * h_q, NP, D);
   if (groups > 0) ws = std::max(ws, split_bytes(s, groups));
   return set_plan(P, T_max, ws, partition_size, num_partitions, workspace_bytes);
@@ -344,7 +346,7 @@ int gqa_decode_impl(const void* q, const void* k_new, const void* v_new, const v
   // The split decode serves the persistent kernel's shapes (and paged caches
   // whose pages hold whole 32-row tiles); the others run on fixed partitions.
   // A window attends over at most `window` positions: plan for that span.
-  const int groups = (!pg.block_table || pg.page_size % 32 == 0) ? gqa_split_groups(s) : 0;
+  const int groups = gqa_split_groups(s, pg.block_table ? pg.page_size : 0);
   const int span = window > 0 && window < T_max ? window : T_max;
   const GqaShape sp{B, h_q, h_kv, D, span, dt};
   const int P = groups > 0 ? attn::kSplitUnit : gqa_auto_partition(sp);

@@ -1022,19 +1022,17 @@ hipError_t launch_one(const GqaArgs& a, int chunks, hipStream_t stream) {
 template <class E, int D>
 hipError_t launch_d(int G, const GqaArgs& a, hipStream_t s) {
   if constexpr (sizeof(typename E::storage) == 2) {
-    // The position-per-lane and matrix-core kernels read a paged cache one
-    // 32-row tile at a time.
-    const bool tiles_fit = a.block_table == nullptr || a.page_size % kPoRows == 0;
-    if (tiles_fit) {
-      switch (G) {
-        case 1: return launch_po<D, 1>(a, s);
-        case 2: return launch_po<D, 2>(a, s);
-        case 4: return launch_po<D, 4>(a, s);
-        case 8: return launch_po<D, 8>(a, s);
-        default:
-          if (gqa_matrix(1, D, G)) return launch_gqa_matrix(D, G, a, 0, false, s);
-          break;
-      }
+    switch (bf16_kernel(D, G, a.block_table ? a.page_size : 0)) {
+      case BfKernel::kMma16: return launch_gqa_mma16(D, G, a, 0, false, s);
+      case BfKernel::kMatrix: return launch_gqa_matrix(D, G, a, 0, false, s);
+      case BfKernel::kPo:
+        switch (G) {
+          case 1: return launch_po<D, 1>(a, s);
+          case 2: return launch_po<D, 2>(a, s);
+          case 4: return launch_po<D, 4>(a, s);
+          default: return launch_po<D, 8>(a, s);
+        }
+      default: break;
     }
   }
   switch (G) {
@@ -1073,8 +1071,21 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const unsigned char* __r
 
 }  // namespace
 
-int gqa_split_groups(int D, int group) {
-  if (gqa_matrix(1, D, group)) return gqa_matrix_groups(D, group);
+// The kernel that serves a bf16 shape (page_size 0: contiguous cache). Paged
+// caches need pages that hold whole tiles of the kernel: 64, 32 or 16 rows
+// for the 16 x 16 matrix-core kernel (groups of up to 16, 32, 64 heads), 32
+// rows for the position-per-lane and the 32 x 32 matrix-core kernels.
+BfKernel bf16_kernel(int D, int group, int page_size) {
+  if (!(D == 64 || D == 128) || !pow2(group)) return BfKernel::kGeneric;
+  const bool fits32 = page_size == 0 || page_size % kPoRows == 0;
+  if (group >= 8 && group <= 64 && (page_size == 0 || page_size % gqa_mma16_tile(group) == 0))
+    return BfKernel::kMma16;
+  if (group <= 8 && fits32) return BfKernel::kPo;
+  if (group >= 16 && group <= 128 && fits32) return BfKernel::kMatrix;
+  return BfKernel::kGeneric;
+}
+
+static int po_split_groups(int D, int group) {
   switch (D * 16 + group) {
     case 128 * 16 + 1: return split_groups_dg<128, 1>();
     case 128 * 16 + 2: return split_groups_dg<128, 2>();
@@ -1088,9 +1099,29 @@ int gqa_split_groups(int D, int group) {
   }
 }
 
+int gqa_split_groups(int D, int group, int page_size) {
+  switch (bf16_kernel(D, group, page_size)) {
+    case BfKernel::kMma16: return gqa_mma16_groups(D, group);
+    case BfKernel::kMatrix: return gqa_matrix_groups(D, group);
+    case BfKernel::kPo: return po_split_groups(D, group);
+    default: return 0;
+  }
+}
+
+int gqa_split_groups_max(int D, int group) {
+  // contiguous caches and pages of 32 rows (the largest page set that can
+  // pick a different kernel)
+  return std::max(gqa_split_groups(D, group, 0), gqa_split_groups(D, group, kPoRows));
+}
+
 hipError_t launch_gqa_split(int D, int group, const GqaArgs& a, int groups, hipStream_t s) {
   if (groups < 1) return hipErrorInvalidValue;
-  if (gqa_matrix(1, D, group)) return launch_gqa_matrix(D, group, a, groups, true, s);
+  switch (bf16_kernel(D, group, a.block_table ? a.page_size : 0)) {
+    case BfKernel::kMma16: return launch_gqa_mma16(D, group, a, groups, true, s);
+    case BfKernel::kMatrix: return launch_gqa_matrix(D, group, a, groups, true, s);
+    case BfKernel::kPo: break;
+    default: return hipErrorInvalidValue;
+  }
   const dim3 grid((unsigned)groups), block(kThreads);
   switch (D * 16 + group) {
     case 128 * 16 + 1: hipLaunchKernelGGL((gqa_partial_po_kernel<128, 1, true>), grid, block, 0, s, a); break;

@@ -103,77 +103,6 @@ __device__ __forceinline__ float partner_half(float v) {
   return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
 }
 
-// A wave-uniform 32-bit load through the scalar cache (read-only data: the
-// sequence lengths and the block table). Waited for at once: as a vector
-// load, the compiler's wait for it would also wait for every tile copy in
-// flight, which it does not know about. p must be wave-uniform.
-__device__ __forceinline__ int sload_i32(const int32_t* p) {
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
-  return v;
-}
-
-// Position in a work-group's tile stream: the current item (segment) and
-// the first position of the current tile. Every wave holds the same values.
-struct Cursor {
-  items::ItemRun run;
-  int len;          // units (or partitions) of the segment
-  int len0;         // seq_lens[b] as stored
-  int n;            // attended length of sequence b
-  int start, end;   // positions [start, end) of the segment
-  int t0;           // current tile
-  bool ok;          // a tile remains
-};
-
-__device__ __forceinline__ int parts_of_len(const GqaArgs& a, int len0) {
-  const int n = attended_len(len0, a.k_new ? 1 : 0, a.T_max);
-  return (int)(((long long)n - window_lo(n, a.window) + a.P - 1) / a.P);
-}
-
-template <bool SPLIT>
-__device__ __forceinline__ void set_item(Cursor& c, const GqaArgs& a) {
-  c.len = SPLIT ? (int)min((long long)(c.run.np - c.run.p), c.run.left) : 1;
-  c.len0 = sload_i32(a.seq_lens + c.run.b);
-  c.n = attended_len(c.len0, a.k_new ? 1 : 0, a.T_max);
-  c.start = window_lo(c.n, a.window) + c.run.p * a.P;
-  c.end = min(c.n - c.start, c.len * a.P) + c.start;
-  c.t0 = c.start;
-}
-
-template <bool SPLIT>
-__device__ __forceinline__ void cursor_init(Cursor& c, const GqaArgs& a) {
-  c.run = items::first_item(a);
-  c.ok = c.run.left > 0 && c.run.b < a.B;
-  if (c.ok) set_item<SPLIT>(c, a);
-}
-
-// Moves to the next tile; returns true when that tile opens a new segment.
-template <bool SPLIT>
-__device__ __forceinline__ bool cursor_next(Cursor& c, const GqaArgs& a) {
-  c.t0 += kTile;
-  if (c.t0 < c.end) return false;
-  if (c.run.left <= c.len) {
-    c.ok = false;
-    return true;
-  }
-  items::ItemRun r = c.run;
-  r.left -= c.len;
-  r.p += c.len;
-  if (r.p >= r.np) {  // the pair is done: next KV head, then the next sequence with positions
-    r.p = 0;
-    if (++r.j >= a.h_kv) {
-      r.j = 0;
-      do {
-        ++r.b;
-      } while (r.b < a.B && (r.np = parts_of_len(a, sload_i32(a.seq_lens + r.b))) == 0);
-    }
-  }
-  c.run = r;
-  c.ok = r.b < a.B;
-  if (c.ok) set_item<SPLIT>(c, a);
-  return true;
-}
-
 template <int D, int G, bool SPLIT>
 __global__ __launch_bounds__((64 * MxCfg<D, G>::kWaves)) void gqa_matrix_kernel(const GqaArgs a) {
   using C = MxCfg<D, G>;
@@ -190,10 +119,10 @@ __global__ __launch_bounds__((64 * MxCfg<D, G>::kWaves)) void gqa_matrix_kernel(
 
   __shared__ __attribute__((aligned(1024))) unsigned char bufs[kRing][C::kBufBytes];
 
-  Cursor cc;  // the tile being computed
-  cursor_init<SPLIT>(cc, a);
+  items::Cursor cc;  // the tile being computed
+  items::cursor_init<SPLIT>(cc, a);
   if (!cc.ok) return;  // an empty run (fewer items than work-groups): uniform exit
-  Cursor pf = cc;      // the tile being copied, three ahead
+  items::Cursor pf = cc;      // the tile being copied, three ahead
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -219,7 +148,7 @@ __global__ __launch_bounds__((64 * MxCfg<D, G>::kWaves)) void gqa_matrix_kernel(
   // slab limited to its attended rows (reads at or past row n return zeros);
   // paged cache, the tile's 32 rows inside its page. Past the run's end a
   // null resource keeps the number of copies per tile fixed.
-  auto tile_src = [&](const Cursor& c, __amdgpu_buffer_rsrc_t& kr, __amdgpu_buffer_rsrc_t& vr,
+  auto tile_src = [&](const items::Cursor& c, __amdgpu_buffer_rsrc_t& kr, __amdgpu_buffer_rsrc_t& vr,
                       uint32_t& soff) {
     if (!c.ok) {
       kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc), 0, 0, kBufWord3);
@@ -235,7 +164,7 @@ __global__ __launch_bounds__((64 * MxCfg<D, G>::kWaves)) void gqa_matrix_kernel(
       soff = (uint32_t)c.t0 * (D * 2);
       return;
     }
-    const int phys = sload_i32(a.block_table + (size_t)b * a.max_pages + (c.t0 >> a.page_shift));
+    const int phys = items::sload_i32(a.block_table + (size_t)b * a.max_pages + (c.t0 >> a.page_shift));
     const bool ok = phys >= 0 && phys < a.num_pages;
     const int rows = ok ? min(kTile, c.n - c.t0) : 0;
     const size_t off = (((size_t)(ok ? phys : 0) * h_kv + j) * a.page_size + (c.t0 & (a.page_size - 1))) * D;
@@ -247,7 +176,7 @@ __global__ __launch_bounds__((64 * MxCfg<D, G>::kWaves)) void gqa_matrix_kernel(
   // The copies of one tile into a buffer: kPerWave 1 KiB blocks per wave,
   // buffer_load_dwordx4 ... lds (M0 holds the LDS address; the compiler is
   // told M0 is clobbered, and it uses M0 for nothing else here).
-  auto issue_tile = [&](unsigned char* buf, const Cursor& c) {
+  auto issue_tile = [&](unsigned char* buf, const items::Cursor& c) {
     __amdgpu_buffer_rsrc_t kr, vr;
     uint32_t soff;
     tile_src(c, kr, vr, soff);
@@ -266,7 +195,7 @@ __global__ __launch_bounds__((64 * MxCfg<D, G>::kWaves)) void gqa_matrix_kernel(
 
   // Decode step: the work-group whose segment holds the new row writes it
   // (K and V) before any copy of the segment's tiles is issued.
-  auto write_new_row = [&](const Cursor& c) {
+  auto write_new_row = [&](const items::Cursor& c) {
     if (!a.k_new || !c.ok) return;
     const int pos = max(c.len0, 0);
     if (pos < T_max && pos >= c.start && pos < c.end) {
@@ -279,7 +208,7 @@ __global__ __launch_bounds__((64 * MxCfg<D, G>::kWaves)) void gqa_matrix_kernel(
   };
   auto copy_and_advance = [&](unsigned char* buf) {
     issue_tile(buf, pf);
-    if (pf.ok && cursor_next<SPLIT>(pf, a) && pf.ok) write_new_row(pf);
+    if (pf.ok && items::cursor_next<SPLIT, kTile>(pf, a) && pf.ok) write_new_row(pf);
   };
 
   write_new_row(pf);
@@ -418,7 +347,7 @@ __global__ __launch_bounds__((64 * MxCfg<D, G>::kWaves)) void gqa_matrix_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
     }
-    cursor_next<SPLIT>(cc, a);
+    items::cursor_next<SPLIT, kTile>(cc, a);
     cur = (cur + 1) & (kRing - 1);
   }
   // The copies issued for the last tiles (zeros into free buffers) land

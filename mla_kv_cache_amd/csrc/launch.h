@@ -41,7 +41,13 @@ hipError_t launch_gqa_partial(int dt, int D, int group, const GqaArgs& a, hipStr
 // partial in slot (work-group + b * h_kv + j): part_out [groups + B*h_kv, G, D],
 // part_lse [groups + B*h_kv, G]. a.P must be kSplitUnit; a.NP is not used.
 constexpr int kSplitUnit = 128;
-int gqa_split_groups(int D, int group);  // work-groups of the split launch on the current device
+// Which kernel serves a bf16 shape (page_size 0: contiguous cache).
+enum class BfKernel { kGeneric, kPo, kMma16, kMatrix };
+BfKernel bf16_kernel(int D, int group, int page_size);
+// Work-groups of the split launch on the current device (0: no split for this
+// shape), and the most any page size of the shape can use (the plan's bound).
+int gqa_split_groups(int D, int group, int page_size);
+int gqa_split_groups_max(int D, int group);
 hipError_t launch_gqa_split(int D, int group, const GqaArgs& a, int groups, hipStream_t stream);
 
 // The matrix-core kernel for bf16 groups of 16 to 128 heads (gqa_matrix.hip):
@@ -50,6 +56,13 @@ hipError_t launch_gqa_split(int D, int group, const GqaArgs& a, int groups, hipS
 // partitions of a.P positions, groups <= 0 picks the resident count).
 int gqa_matrix_groups(int D, int group);
 hipError_t launch_gqa_matrix(int D, int group, const GqaArgs& a, int groups, bool split, hipStream_t stream);
+
+// The 16 x 16 matrix-core kernel for bf16 groups of 1 to 64 heads
+// (gqa_mma16.hip): positions per tile for a group size, work-groups of a
+// split launch, and the launch (same conventions as launch_gqa_matrix).
+int gqa_mma16_tile(int group);
+int gqa_mma16_groups(int D, int group);
+hipError_t launch_gqa_mma16(int D, int group, const GqaArgs& a, int groups, bool split, hipStream_t stream);
 // Merge of the split partials into out [B, h_kv * group, D].
 hipError_t launch_split_merge(int out_dt, const float* part_out, const float* part_lse,
                               const int32_t* seq_lens, int len_add, int window, int B, int h_kv,

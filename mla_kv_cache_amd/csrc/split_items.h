@@ -110,5 +110,76 @@ __device__ __forceinline__ void next_item(ItemRun& r, const GqaArgs& a) {
   } while (r.b < a.B && (r.np = partitions_of(a, r.b)) == 0);
 }
 
+// A wave-uniform 32-bit load through the scalar cache (read-only data: the
+// sequence lengths and the block table). Waited for at once: as a vector
+// load, the compiler's wait for it would also wait for every tile copy in
+// flight, which it does not know about. p must be wave-uniform.
+__device__ __forceinline__ int sload_i32(const int32_t* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
+// Position in a work-group's tile stream: the current item (segment) and
+// the first position of the current tile. Every wave holds the same values.
+struct Cursor {
+  items::ItemRun run;
+  int len;          // units (or partitions) of the segment
+  int len0;         // seq_lens[b] as stored
+  int n;            // attended length of sequence b
+  int start, end;   // positions [start, end) of the segment
+  int t0;           // current tile
+  bool ok;          // a tile remains
+};
+
+__device__ __forceinline__ int parts_of_len(const GqaArgs& a, int len0) {
+  const int n = attended_len(len0, a.k_new ? 1 : 0, a.T_max);
+  return (int)(((long long)n - window_lo(n, a.window) + a.P - 1) / a.P);
+}
+
+template <bool SPLIT>
+__device__ __forceinline__ void set_item(Cursor& c, const GqaArgs& a) {
+  c.len = SPLIT ? (int)min((long long)(c.run.np - c.run.p), c.run.left) : 1;
+  c.len0 = sload_i32(a.seq_lens + c.run.b);
+  c.n = attended_len(c.len0, a.k_new ? 1 : 0, a.T_max);
+  c.start = window_lo(c.n, a.window) + c.run.p * a.P;
+  c.end = min(c.n - c.start, c.len * a.P) + c.start;
+  c.t0 = c.start;
+}
+
+template <bool SPLIT>
+__device__ __forceinline__ void cursor_init(Cursor& c, const GqaArgs& a) {
+  c.run = items::first_item(a);
+  c.ok = c.run.left > 0 && c.run.b < a.B;
+  if (c.ok) set_item<SPLIT>(c, a);
+}
+
+// Moves to the next tile of TILE positions; returns true when that tile opens a new segment.
+template <bool SPLIT, int TILE>
+__device__ __forceinline__ bool cursor_next(Cursor& c, const GqaArgs& a) {
+  c.t0 += TILE;
+  if (c.t0 < c.end) return false;
+  if (c.run.left <= c.len) {
+    c.ok = false;
+    return true;
+  }
+  items::ItemRun r = c.run;
+  r.left -= c.len;
+  r.p += c.len;
+  if (r.p >= r.np) {  // the pair is done: next KV head, then the next sequence with positions
+    r.p = 0;
+    if (++r.j >= a.h_kv) {
+      r.j = 0;
+      do {
+        ++r.b;
+      } while (r.b < a.B && (r.np = parts_of_len(a, sload_i32(a.seq_lens + r.b))) == 0);
+    }
+  }
+  c.run = r;
+  c.ok = r.b < a.B;
+  if (c.ok) set_item<SPLIT>(c, a);
+  return true;
+}
+
 }  // namespace items
 }  // namespace attn

@@ -20,7 +20,8 @@ static hipError_t reached() {
 }
 
 // No device: the work-balanced split is not planned (as on a host without a GPU).
-int gqa_split_groups(int, int) { return 0; }
+int gqa_split_groups(int, int, int) { return 0; }
+int gqa_split_groups_max(int, int) { return 0; }
 
 hipError_t launch_gqa_partial(int, int, int, const GqaArgs&, hipStream_t) { return reached(); }
 hipError_t launch_gqa_split(int, int, const GqaArgs&, int, hipStream_t) { return reached(); }

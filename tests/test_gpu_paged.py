@@ -71,6 +71,9 @@ CASES = [
     (2, 128, 2, 64, 8, 32, torch.bfloat16, [256, 77]),
     (2, 64, 1, 128, 32, 16, torch.bfloat16, [500, 17]),          # 16-row pages: chunks of 16 heads
     (2, 32, 1, 64, 10, 32, torch.float32, [300, 12]),
+    (2, 32, 2, 128, 20, 32, torch.bfloat16, [640, 100]),        # groups of 16 in 32-row pages
+    (2, 16, 1, 64, 40, 16, torch.bfloat16, [640, 5]),           # groups of 16 in 16-row pages
+    (2, 16, 2, 128, 8, 64, torch.bfloat16, [500, 64]),          # groups of 8 in 64-row pages
     (2, 16, 4, 128, 8, 64, torch.float32, [512, 200]),
     (2, 16, 8, 64, 20, 16, torch.float32, [320, 100]),
 ]

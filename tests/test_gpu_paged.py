@@ -56,6 +56,23 @@ def _paginate_kv(cache, lens, page_size, seed, spare=3):
     return pages, table
 
 
+def _kernel(dt, D, g, ps):
+    """Which kernel serves a shape (page size 0: contiguous), as the library's header states it:
+    bf16 groups of 8 to 64 on 16 x 16 matrix-core tiles of 64, 32 or 16 positions (groups up to
+    16, 32, 64), groups up to 8 position-per-lane and groups of 16 to 128 on 32 x 32 tiles (pages
+    of 32 rows), anything else per row."""
+    if dt == torch.float32:
+        return "generic"
+    tile16 = 64 if g <= 16 else (32 if g == 32 else 16)
+    if 8 <= g <= 64 and (ps == 0 or ps % tile16 == 0):
+        return "mma16"
+    if g <= 8 and ps % 32 == 0:
+        return "po"
+    if 16 <= g <= 128 and ps % 32 == 0:
+        return "matrix"
+    return "generic"
+
+
 CASES = [
     # (B, h_q, h_kv, D, max_pages, page_size, dtype, lens)
     (3, 8, 2, 128, 16, 64, torch.bfloat16, [1024, 517, 1]),
@@ -90,9 +107,10 @@ def test_paged_matches_contiguous_and_oracle(gpu, case):
     vp, _ = _paginate_kv(v, lens, ps, 1)
     out = m.attn_decode_gqa_paged(q.to(gpu), kp.to(gpu), vp.to(gpu), table.to(gpu), l.to(gpu), scale=w.scale)
     lin = m.attn_decode_gqa(q.to(gpu), k.to(gpu), v.to(gpu), l.to(gpu), scale=w.scale)
-    # bf16 pages shorter than a 32-row tile take the per-row kernel, whose
-    # reduction order differs from the contiguous bf16 kernel's: tolerance only
-    same_kernel = dt == torch.float32 or h_q // h_kv == 16 or ps % 32 == 0
+    # The paged decode runs the contiguous decode's arithmetic in its order
+    # when both take the same kernel (bit-identical); pages that do not hold
+    # whole tiles of that kernel take another one: tolerance only.
+    same_kernel = _kernel(dt, D, h_q // h_kv, ps) == _kernel(dt, D, h_q // h_kv, 0)
     if same_kernel:
         assert torch.equal(_bits(out), _bits(lin))
     ref = oracle.decode_gqa_paged(q, kp, vp, table, l, w.scale, ps)

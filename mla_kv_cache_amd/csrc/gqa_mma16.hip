@@ -9,7 +9,7 @@
 //   S^T [16 positions x 16 heads]  = K [16 x D] . Q^T [D x 16]    (16x16x32 bf16, D / 32 steps)
 //   O^T [D x 16 heads]            += V^T [D x 16] . P^T [16 x 16]  (16x16x16 bf16, D / 16 tiles)
 //
-// A groups of fewer than 16 heads fills part of the head columns (the rest
+// A group of fewer than 16 heads fills part of the head columns (the rest
 // multiply zeros and are never stored); on these tiles the products cost a
 // few hundred matrix-core cycles per 8 KiB of K and V, far below the time
 // HBM takes to deliver them, and the softmax handles 4 values per lane.
@@ -78,7 +78,7 @@ struct M16 {
   static constexpr int kPerWave = kBlocks / kWaves;
   static constexpr int kRowsPerBlock = 1024 / (2 * D);
   static constexpr int kPitch = D * 4 + 16;             // combine-area row (fp32, padded)
-  static constexpr int kAreas = kNS == 4 ? 2 : (kNS == 2 ? kNB : 0);
+  static constexpr int kAreas = kNS == 4 ? 2 : (kNS == 2 ? 1 : 0);  // the head blocks of ns = 2 take turns
   static_assert(kNB * kNS == kWaves, "waves = head blocks x sub-tiles");
   static_assert(kBlocks % kWaves == 0, "every wave copies the same number of blocks");
 };
@@ -328,9 +328,14 @@ __global__ __launch_bounds__(64 * kWaves) void gqa_mma16_kernel(const GqaArgs a)
         __syncthreads();
         if (st == 0) add(0);
       } else if constexpr (C::kNS == 2) {
-        if (st == 1) put(hb);
-        __syncthreads();
-        if (st == 0) add(hb);
+        // one area, the head blocks in turn (keeps two work-groups per CU)
+#pragma unroll
+        for (int hb2 = 0; hb2 < C::kNB; ++hb2) {
+          if (st == 1 && hb == hb2) put(0);
+          __syncthreads();
+          if (st == 0 && hb == hb2) add(0);
+          __syncthreads();
+        }
       }
       if (st == 0 && hvalid) {
         const int b = cc.run.b, j = cc.run.j;

@@ -81,16 +81,19 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void absorb_q_kernel(
   }
 }
 
-constexpr int kUpRows = 128;              // W_UV rows (contraction) per LDS chunk
-constexpr int kUpCols = 32 * kWavesPerGroup;   // W_UV columns per work-group
+constexpr int kUpWaves = 2;                     // waves per work-group, 32 output columns each
+constexpr int kUpCols = 32 * kUpWaves;          // W_UV columns per work-group (128-byte row pieces)
 constexpr int kUpPitch = kUpCols * 2 + 32;      // bytes per LDS row: padding spreads the transposed reads
+constexpr int kUpMaxRows = 512;                 // the whole contraction of one head fits in LDS
 
-// One work-group per (head, 128 output columns), one wave per 32 of them;
-// W_UV is staged through LDS 128 rows at a time.
-__global__ __launch_bounds__(64 * kWavesPerGroup) void up_v_kernel(
+// One work-group per (head, 64 output columns), one wave per 32 of them. The
+// head's whole W_UV slice [d_c x 64] is loaded into LDS at once (every load in
+// flight together, one barrier), then each wave runs the full contraction.
+// d_c > 512 takes the slice in pieces of 512 rows.
+__global__ __launch_bounds__(64 * kUpWaves) void up_v_kernel(
     const uint16_t* __restrict__ o_lat, const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ out,
     int B, int H, int d_c, int d_v) {
-  __shared__ __attribute__((aligned(16))) unsigned char wt[kUpRows * kUpPitch];
+  __shared__ __attribute__((aligned(16))) unsigned char wt[kUpMaxRows * kUpPitch];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int h = blockIdx.y;
@@ -111,14 +114,16 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void up_v_kernel(
     for (int t = 0; t < kMTilesPerPass; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-    for (int kc = 0; kc < d_c; kc += kUpRows) {
-      const int rows = min(kUpRows, d_c - kc);   // a multiple of 16
-      __syncthreads();                           // the previous chunk's reads are done
-      for (int i = threadIdx.x; i < rows * (cols / 8); i += blockDim.x) {
-        const int r = i / (cols / 8), c8 = i % (cols / 8);
-        *reinterpret_cast<uint4*>(wt + r * kUpPitch + c8 * 16) = ld16(wsrc + (size_t)(kc + r) * d_v + c8 * 8);
+    for (int kc = 0; kc < d_c; kc += kUpMaxRows) {
+      const int rows = min(kUpMaxRows, d_c - kc);   // a multiple of 16
+      if (mt0 > 0 || kc > 0) __syncthreads();       // the previous piece's reads are done
+      if (mt0 == 0 || d_c > kUpMaxRows) {
+        for (int i = threadIdx.x; i < rows * (cols / 8); i += blockDim.x) {
+          const int r = i / (cols / 8), c8 = i % (cols / 8);
+          *reinterpret_cast<uint4*>(wt + r * kUpPitch + c8 * 16) = ld16(wsrc + (size_t)(kc + r) * d_v + c8 * 8);
+        }
+        __syncthreads();
       }
-      __syncthreads();
       if (active) {
         for (int k0 = 0; k0 < rows; k0 += 16) {
           const unsigned char* base = wt + (k0 + tr_row) * kUpPitch + tr_col * 2;
@@ -159,7 +164,7 @@ hipError_t launch_absorb_q(const void* q, const void* w_uk, void* q_lat, int B, 
 hipError_t launch_up_v(const void* o_lat, const void* w_uv, void* out, int B, int H, int d_c, int d_v,
                        hipStream_t stream) {
   const dim3 grid((d_v + kUpCols - 1) / kUpCols, H);
-  hipLaunchKernelGGL(up_v_kernel, grid, dim3(64 * kWavesPerGroup), 0, stream,
+  hipLaunchKernelGGL(up_v_kernel, grid, dim3(64 * kUpWaves), 0, stream,
                      static_cast<const uint16_t*>(o_lat), static_cast<const uint16_t*>(w_uv),
                      static_cast<uint16_t*>(out), B, H, d_c, d_v);
   return hipGetLastError();

@@ -36,6 +36,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWavesPerGroup = 4;
 constexpr int kMTilesPerPass = 2;  // 32-row M tiles accumulated at once (64 registers)
+constexpr int kChunk = 8;          // k-steps whose operand loads are issued together
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -66,14 +67,25 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void absorb_q_kernel(
     for (int t = 0; t < kMTilesPerPass; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-    for (int k0 = 0; k0 < d_h; k0 += 16) {
-      const uint4 bw = ld16(wrow + k0);
+    // Eight k-steps at a time: every fragment load of the chunk is issued
+    // before its products, so the chunk costs one memory round trip.
+    for (int kb = 0; kb < d_h; kb += 16 * kChunk) {
+      uint4 bw[kChunk], aq[kChunk][kMTilesPerPass];
 #pragma unroll
-      for (int t = 0; t < kMTilesPerPass; ++t) {
-        const int m = (mt0 + t) * 32 + (lane % 32);
-        const uint4 aq = m < B ? ld16(q + ((size_t)m * H + h) * d_h + k0 + ko) : make_uint4(0, 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aq), as_bf16x8(bw), acc[t], 0, 0, 0);
+      for (int i = 0; i < kChunk; ++i) {
+        const int k0 = kb + 16 * i;
+        bw[i] = k0 < d_h ? ld16(wrow + k0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < kMTilesPerPass; ++t) {
+          const int m = (mt0 + t) * 32 + (lane % 32);
+          aq[i][t] = (m < B && k0 < d_h) ? ld16(q + ((size_t)m * H + h) * d_h + k0 + ko) : make_uint4(0, 0, 0, 0);
+        }
       }
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i)
+#pragma unroll
+        for (int t = 0; t < kMTilesPerPass; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aq[i][t]), as_bf16x8(bw[i]), acc[t], 0, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < kMTilesPerPass; ++t)
@@ -125,18 +137,32 @@ __global__ __launch_bounds__(64 * kUpWaves) void up_v_kernel(
         __syncthreads();
       }
       if (active) {
-        for (int k0 = 0; k0 < rows; k0 += 16) {
-          const unsigned char* base = wt + (k0 + tr_row) * kUpPitch + tr_col * 2;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 4 * kUpPitch));
-          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-          const uint4 bw = make_uint4(l2.x, l2.y, h2.x, h2.y);
+        // Eight k-steps at a time: the o_lat fragment loads of the chunk are
+        // issued together, then the products (one memory round trip per chunk).
+        for (int kb = 0; kb < rows; kb += 16 * kChunk) {
+          uint4 ao[kChunk][kMTilesPerPass];
 #pragma unroll
-          for (int t = 0; t < kMTilesPerPass; ++t) {
-            const int m = (mt0 + t) * 32 + (lane % 32);
-            const uint4 ao = m < B ? ld16(o_lat + ((size_t)m * H + h) * d_c + kc + k0 + ko)
-                                   : make_uint4(0, 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ao), as_bf16x8(bw), acc[t], 0, 0, 0);
+          for (int i = 0; i < kChunk; ++i) {
+            const int k0 = kb + 16 * i;
+#pragma unroll
+            for (int t = 0; t < kMTilesPerPass; ++t) {
+              const int m = (mt0 + t) * 32 + (lane % 32);
+              ao[i][t] = (m < B && k0 < rows) ? ld16(o_lat + ((size_t)m * H + h) * d_c + kc + k0 + ko)
+                                               : make_uint4(0, 0, 0, 0);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < kChunk; ++i) {
+            const int k0 = kb + 16 * i;
+            if (k0 >= rows) break;
+            const unsigned char* base = wt + (k0 + tr_row) * kUpPitch + tr_col * 2;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 4 * kUpPitch));
+            const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+            const uint4 bw = make_uint4(l2.x, l2.y, h2.x, h2.y);
+#pragma unroll
+            for (int t = 0; t < kMTilesPerPass; ++t)
+              acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ao[i][t]), as_bf16x8(bw), acc[t], 0, 0, 0);
           }
         }
       }

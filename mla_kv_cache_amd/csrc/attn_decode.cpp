@@ -379,6 +379,13 @@ int gqa_decode_impl(const void* q, const void* k_new, const void* v_new, const v
     return ATTN_OK;
   }
   if (stages != 3) return ATTN_ERR_UNSUPPORTED;
+  if (NP == 1) {  // one partition: the partial kernel writes the output itself, no merge
+    attn::GqaArgs d = a;
+    d.out = out;
+    d.out_bf16 = dt == ATTN_BF16;
+    if (attn::launch_gqa_partial(int(dt), D, h_q / h_kv, d, stream) != hipSuccess) return ATTN_ERR_HIP;
+    return ATTN_OK;
+  }
   if (attn::launch_gqa_partial(int(dt), D, h_q / h_kv, a, stream) != hipSuccess) return ATTN_ERR_HIP;
   if (attn::launch_merge(int(dt), part_out, part_lse, seq_lens, k_new ? 1 : 0, window, B, h_q, D,
                          T_max, P, NP, out, stream) != hipSuccess)

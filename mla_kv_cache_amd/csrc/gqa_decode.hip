@@ -101,7 +101,16 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const GqaArgs a) 
   const int len0 = a.seq_lens[b];
   const int n = attended_len(len0, a.k_new ? 1 : 0, T_max);
   const int start = window_lo(n, a.window) + p * P;
-  if (start >= n) return;  // no position in this partition: nothing written, the merge skips it
+  if (start >= n) {  // no position in this partition: nothing written, the merge skips it
+    if (a.out) {     // single partition written as the output: an empty row is zeros
+      const size_t orow = ((size_t)b * h_kv * GG + (size_t)j * GG + (size_t)hc * G) * D;
+      for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+        if (a.out_bf16) static_cast<uint16_t*>(a.out)[orow + idx] = 0;
+        else static_cast<float*>(a.out)[orow + idx] = 0.f;
+      }
+    }
+    return;
+  }
   const int end = min(start, n - P) + P;  // = min(start + P, n) without overflow
   if (a.k_new) {  // decode step: the work-group that reads the new row writes it first
     const int pos = max(len0, 0);
@@ -257,6 +266,12 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const GqaArgs a) 
       const float f = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
       L += sm_l[w][h] * f;
       A += sm_acc[w][h][d] * f;
+    }
+    if (a.out) {  // the only partition: finished output row
+      const size_t orow = (size_t)b * H + (size_t)j * GG + (size_t)hc * G + h;
+      if (a.out_bf16) static_cast<uint16_t*>(a.out)[orow * D + d] = f32_to_bf16_rne(A / L);
+      else static_cast<float*>(a.out)[orow * D + d] = A / L;
+      continue;
     }
     const size_t row = ((size_t)b * H + (size_t)j * GG + (size_t)hc * G + h) * NP + p;
     part_out[row * D + d] = A / L;

@@ -30,6 +30,11 @@ struct GqaArgs {
   // Generic kernel only (set by its launcher): the query heads of a group are
   // taken in head_chunks work-groups of group / head_chunks heads each.
   int head_chunks;
+  // Generic kernel with one partition (NP == 1) only: when out is set, the
+  // kernel writes the finished rows to out [B, h_q, D] (bf16 when out_bf16,
+  // else fp32; empty rows as zeros) instead of partials, and no merge runs.
+  void* out;
+  int out_bf16;
 };
 
 hipError_t launch_gqa_partial(int dt, int D, int group, const GqaArgs& a, hipStream_t stream);

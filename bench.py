@@ -194,11 +194,14 @@ def summarize_counters(csvs, trace_csv=None):
     """Markdown table of per-dispatch hardware counters averaged per kernel, from
     rocprofv3 --pmc counter_collection CSVs (one or more passes).
 
-    Derived columns (MI355X: 8 XCDs, 256 CUs, 1,024 SIMDs):
-      cycles per dispatch = GRBM_GUI_ACTIVE / 8 (the counter sums the 8 XCDs);
+    Derived columns (MI355X: 32 shader engines, 256 CUs, 1,024 SIMDs):
+      cycles = SQ_BUSY_CYCLES / 32 (cycles with waves present, summed over the
+        32 shader engines: the kernel's duration in cycles when it fills the chip);
+      MHz = cycles / the kernel-trace duration (the clock the kernel ran at);
       MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1,024 SIMDs x cycles);
-      VALU busy = 4 x SQ_ACTIVE_INST_VALU / (1,024 x cycles) (quad-cycles of VALU issue, per SIMD);
-      LDS bank-conflict share = SQ_LDS_BANK_CONFLICT / (4 x SQ_ACTIVE_INST_LDS);
+      VALU issue = 4 x SQ_ACTIVE_INST_VALU / (1,024 x cycles) (quad-cycles waves spend
+        issuing VALU instructions, summed over waves, per SIMD-cycle);
+      LDS bank conflicts = SQ_LDS_BANK_CONFLICT / (256 CUs x cycles) (stalled cycles per CU-cycle);
       L2 hit rate = TCC_HIT / (TCC_HIT + TCC_MISS)."""
     import csv
     per = {}
@@ -222,16 +225,17 @@ def summarize_counters(csvs, trace_csv=None):
         v = d.get(c)
         return sum(v.values()) / len(v) if v else None
 
-    lines = ["| Kernel | dispatches | us (trace) | cycles / dispatch | MHz | MFMA busy | VALU busy | "
-             "LDS bank-conflict share | L2 hit rate |",
+    lines = ["| Kernel | dispatches | us (trace) | cycles / dispatch | MHz | MFMA busy | VALU issue | "
+             "LDS bank conflicts | L2 hit rate |",
              "|---|---|---|---|---|---|---|---|---|"]
     for name, d in sorted(per.items()):
-        gui = avg(d, "GRBM_GUI_ACTIVE")
-        cyc = gui / 8 if gui else None
+        busy = avg(d, "SQ_BUSY_CYCLES")
+        cyc = busy / 32 if busy else None
         us = sum(dur[name]) / len(dur[name]) if name in dur else None
         mfma, valu = avg(d, "SQ_VALU_MFMA_BUSY_CYCLES"), avg(d, "SQ_ACTIVE_INST_VALU")
         bank, lds = avg(d, "SQ_LDS_BANK_CONFLICT"), avg(d, "SQ_ACTIVE_INST_LDS")
-        hit, miss = avg(d, "TCC_HIT"), avg(d, "TCC_MISS")
+        hit = avg(d, "TCC_HIT") if "TCC_HIT" in d else avg(d, "TCC_HIT_sum")
+        miss = avg(d, "TCC_MISS") if "TCC_MISS" in d else avg(d, "TCC_MISS_sum")
         ndisp = max(len(v) for v in d.values())
         f = lambda x, fmt: (fmt.format(x) if x is not None else "-")
         lines.append("| `{}` | {} | {} | {} | {} | {} | {} | {} | {} |".format(
@@ -239,7 +243,7 @@ def summarize_counters(csvs, trace_csv=None):
             f(cyc / us if cyc and us else None, "{:,.0f}"),
             f(mfma / (1024 * cyc) if mfma is not None and cyc else None, "{:.1%}"),
             f(4 * valu / (1024 * cyc) if valu is not None and cyc else None, "{:.1%}"),
-            f(bank / (4 * lds) if bank is not None and lds else None, "{:.2%}"),
+            f(bank / (256 * cyc) if bank is not None and cyc else None, "{:.2%}"),
             f(hit / (hit + miss) if hit is not None and miss is not None and hit + miss > 0 else None, "{:.1%}")))
     raw = ["", "Raw averages per dispatch:", "",
            "| Kernel | " + " | ".join(sorted({c for d in per.values() for c in d})) + " |",

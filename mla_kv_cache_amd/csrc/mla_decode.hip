@@ -477,24 +477,29 @@ void mla_partial_kernel(const MlaArgs a) {
   // would otherwise be written back while the next kernel streams its cache.
   // The staging area is this wave's own blocks of the buffer after the last
   // tile's: no other wave reads that buffer any more, and this wave's copies
-  // into it have landed.
+  // into it have landed. In block k, head 8k + c holds the eight 16-byte
+  // pieces of its 32 dims in chunks 8c .. 8c + 7, piece x at chunk
+  // 8c + (x ^ phi(8k + c)): with phi below, the 16 lanes of each write
+  // group (16 heads, one piece each) land in 16 different bank groups.
   static_assert(TC::kPerWave >= 4, "the staging area is four of this wave's copy blocks");
   unsigned char* stage = bufs[cur];
-  const int sh = lane >> 3, sc = lane & 7;  // the head (within 8) and 16-byte piece this lane stores
+  auto phi = [](int c) { return ((c >> 1) & 3) | (((c >> 3) & 1) << 2); };
+  const int sh = lane >> 3, sc = lane & 7;  // the head (within 8) and stored piece this lane reads
+  const int wphi = phi(col);
   const size_t prow0 = ((size_t)b * H + hb * (32 * NW) + wave * 32) * NP + p;
 #pragma unroll
   for (int t = 0; t < kOTiles; ++t) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      float4* dst = reinterpret_cast<float4*>(stage + 1024 * (wave + NW * (col >> 3)) + 128 * (col & 7) +
-                                              4 * (8 * g + 4 * half));
+      float4* dst = reinterpret_cast<float4*>(stage + 1024 * (wave + NW * (col >> 3)) +
+                                              16 * (8 * (col & 7) + ((2 * g + half) ^ wphi)));
       *dst = make_float4(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv, acc[t][4 * g + 2] * inv,
                          acc[t][4 * g + 3] * inv);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(stage + 1024 * (wave + NW * k) + 16 * lane);
-      float* po = part_out + (prow0 + (size_t)(8 * k + sh) * NP) * kDc + 32 * t + 4 * sc;
+      float* po = part_out + (prow0 + (size_t)(8 * k + sh) * NP) * kDc + 32 * t + 4 * (sc ^ phi(8 * k + sh));
       __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(po));
     }
   }

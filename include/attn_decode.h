@@ -51,14 +51,19 @@
  *   points expose the two stages (for a caller that merges partials itself,
  *   e.g. across devices); the one-call entry points run both with the
  *   library's own partition size and a caller-provided workspace.
- * - bf16 GQA with D in {64, 128} and g in {1, 2, 4, 8} (contiguous caches, and
- *   paged caches whose pages are a multiple of 32 positions) is split
- *   differently by the one-call entry points: every resident work-group takes
- *   an equal share of all (sequence, KV head, 128-position unit) work, and
- *   each work-group's share of a (sequence, KV head) row is one partial. The
- *   cut points then depend on the sequence lengths and on the device's
- *   compute-unit count; on one device the output is still bit-identical
- *   from run to run.
+ * - bf16 GQA (every supported g; contiguous caches, and paged caches whose
+ *   pages hold at least 32 positions, 16 at g = 64) is split differently
+ *   by the one-call entry points: every resident work-group takes an equal
+ *   share of all (sequence, KV head, 128-position unit) work, and each
+ *   work-group's share of a (sequence, KV head) row is one partial. The cut
+ *   points then depend on the sequence lengths and on the device's compute-
+ *   unit count; on one device the output is still bit-identical from run to
+ *   run. Which kernel runs is a function of (D, g, page size): g <= 4 streams
+ *   one position per lane on the vector ALUs; g = 8 to 64 scores and sums on
+ *   16x16 matrix-core tiles; g = 128 on 32x32 tiles (a paged cache picks
+ *   among them by which tile its pages hold whole). fp32 caches, and bf16
+ *   pages too small for any of those tiles, run on fixed partitions through
+ *   a generic kernel.
  * - Host state: the library keeps, per device index, the device's compute-
  *   unit count, and per process the resident work-groups per compute unit of
  *   each persistent kernel (a property of the kernel on gfx950), both read
@@ -124,10 +129,12 @@ uint64_t attn_mla_cache_bytes(uint64_t n_layers, uint64_t d_c, uint64_t d_r,
  * v_cache  [B, h_kv, T_max, D]   dtype dt
  * seq_lens int32 [B]
  * out      [B, h_q, D]           dtype dt
- * Supported: D in {64, 128}; g = h_q / h_kv in {1, 2, 4, 8, 16}; dt in
- * {ATTN_F32, ATTN_BF16}. Any B >= 1, T_max >= 1 with B*h_kv*T_max*D < 2^40;
- * one (sequence, KV head) slab, T_max*D*sizeof(elem), must stay below 2 GiB
- * (ATTN_ERR_UNSUPPORTED otherwise).
+ * Supported: D in {64, 128}; g = h_q / h_kv a power of two up to 128 (MHA
+ * g = 1; MQA h_kv = 1 with h_q up to 128; other g: ATTN_ERR_UNSUPPORTED); dt
+ * in {ATTN_F32, ATTN_BF16}. B, h_kv and h_kv * max(1, g / 16) at most 65535
+ * (ATTN_ERR_INVALID_ARG otherwise). Any B >= 1, T_max >= 1 with
+ * B*h_kv*T_max*D < 2^40; one (sequence, KV head) slab, T_max*D*sizeof(elem),
+ * must stay below 2 GiB (ATTN_ERR_UNSUPPORTED otherwise).
  */
 
 /* The library's plan for a shape: partition size (positions per split, as
@@ -151,8 +158,7 @@ int attn_decode_gqa(const void* q, const void* k_cache, const void* v_cache,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The two stages of attn_decode_gqa where it runs the work-balanced split
- * (bf16, D in {64, 128}, g in {1, 2, 4, 8}; ATTN_ERR_UNSUPPORTED for other
- * shapes). They take exactly attn_decode_gqa's arguments and checks.
+ * (bf16 storage, every supported D and g; ATTN_ERR_UNSUPPORTED for fp32). They take exactly attn_decode_gqa's arguments and checks.
  * attn_decode_gqa_split runs stage 1 only: it writes the partials into the
  * workspace and does not touch `out`. attn_decode_gqa_split_merge runs stage 2
  * only: it reads those partials and seq_lens (which must not have changed)
@@ -238,8 +244,9 @@ int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_
  * A sequence holds at most T_max = max_pages * page_size positions (seq_lens
  * clamped to it); entries past a sequence's last used page are never read,
  * and pages may be shared between sequences (read-only here). page_size: a
- * power of two >= 16; the fast bf16 kernel (g <= 8) needs a multiple of 32,
- * 16-row pages go through a slower per-row gather. A used table entry outside
+ * power of two >= 16; the bf16 split kernels need pages of at least 32 rows
+ * (16 at g = 64); smaller pages go through the generic kernel's per-row
+ * gather (slower). A used table entry outside
  * [0, num_pages) never faults: its rows read as zeros (or as a clamped page on
  * the per-row path) and the result for that sequence is unspecified.
  * Workspace: attn_decode_gqa_workspace_bytes(B, h_q, h_kv, D, T_max, dt). */

@@ -189,7 +189,7 @@ def _gqa_split_call(fn_name, q, k_cache, v_cache, seq_lens, workspace, scale, ou
 
 def attn_decode_gqa_split(q, k_cache, v_cache, seq_lens, workspace: torch.Tensor,
                           scale: Optional[float] = None, out: Optional[torch.Tensor] = None):
-    """Stage 1 of attn_decode_gqa's work-balanced split (bf16, D in {64,128}, g in {1,2,4,8}):
+    """Stage 1 of attn_decode_gqa's work-balanced split (bf16 storage, every supported D and g):
     writes the partials into `workspace` (attn_decode_gqa_workspace_bytes bytes); `out` is
     checked, not written."""
     _gqa_split_call("attn_decode_gqa_split", q, k_cache, v_cache, seq_lens, workspace, scale, out)

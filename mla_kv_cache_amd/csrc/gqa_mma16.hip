@@ -14,8 +14,8 @@
 // few hundred matrix-core cycles per 8 KiB of K and V, far below the time
 // HBM takes to deliver them, and the softmax handles 4 values per lane.
 //
-// Work-group: 4 waves; nb = max(1, G / 16) blocks of 16 heads, ns = 4 / nb
-// sub-tiles per tile. A tile is 16 ns positions of one (sequence, KV head),
+// Work-group: 4 waves (8 at G = 32); nb = max(1, G / 16) blocks of 16 heads,
+// ns = waves / nb sub-tiles per tile. A tile is 16 ns positions of one (sequence, KV head),
 // copied from HBM once into a ring of four LDS buffers (buffer-to-LDS copies,
 // three tiles ahead), and wave w takes head block w % nb and sub-tile w / nb:
 // every score and weight is computed once. The waves meet once per tile, to
@@ -59,12 +59,14 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kWaves = 4;
 constexpr int kRing = 4;
 constexpr float kTau = 8.0f;
 
 template <int D, int G>
 struct M16 {
+  // Waves per work-group: 4, or 8 at G = 32 (one work-group per CU with two
+  // waves per SIMD, 64-position tiles).
+  static constexpr int kWaves = G == 32 ? 8 : 4;
   static constexpr int kNB = G <= 16 ? 1 : G / 16;      // blocks of 16 heads
   static constexpr int kHV = G < 16 ? G : 16;           // valid heads per block
   static constexpr int kNS = kWaves / kNB;              // 16-position sub-tiles per tile
@@ -98,8 +100,9 @@ __device__ __forceinline__ float head_max(float x) { return xor32_max(xor16_max(
 __device__ __forceinline__ float head_sum(float x) { return xor32_sum(xor16_sum(x)); }
 
 template <int D, int G, bool SPLIT>
-__global__ __launch_bounds__(64 * kWaves) void gqa_mma16_kernel(const GqaArgs a) {
+__global__ __launch_bounds__((64 * M16<D, G>::kWaves)) void gqa_mma16_kernel(const GqaArgs a) {
   using C = M16<D, G>;
+  constexpr int kWaves = C::kWaves;
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
   // Not restrict: a decode step writes one row of each cache before reading it.
   const uint16_t* kc = static_cast<const uint16_t*>(a.k);
@@ -319,7 +322,7 @@ __global__ __launch_bounds__(64 * kWaves) void gqa_mma16_kernel(const GqaArgs a)
 #pragma unroll
         for (int t = 0; t < C::kOT; ++t) acc[t] += *reinterpret_cast<const f32x4*>(base + 64 * t);
       };
-      if constexpr (C::kNS == 4) {
+      if constexpr (C::kNS == 4 && C::kNB == 1) {
         if (st >= 2) put(st - 2);
         __syncthreads();
         if (st < 2) add(st);
@@ -327,6 +330,19 @@ __global__ __launch_bounds__(64 * kWaves) void gqa_mma16_kernel(const GqaArgs a)
         if (st == 1) put(0);
         __syncthreads();
         if (st == 0) add(0);
+      } else if constexpr (C::kNS == 4) {
+        // two areas, the head blocks in turn
+#pragma unroll
+        for (int hb2 = 0; hb2 < C::kNB; ++hb2) {
+          if (hb == hb2 && st >= 2) put(st - 2);
+          __syncthreads();
+          if (hb == hb2 && st < 2) add(st);
+          __syncthreads();
+          if (hb == hb2 && st == 1) put(0);
+          __syncthreads();
+          if (hb == hb2 && st == 0) add(0);
+          __syncthreads();
+        }
       } else if constexpr (C::kNS == 2) {
         // one area, the head blocks in turn (keeps two work-groups per CU)
 #pragma unroll
@@ -376,7 +392,7 @@ int m16_per_cu() {
   static const int per_cu = [] {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&gqa_mma16_kernel<D, G, SPLIT>),
-                                                     64 * kWaves, 0) != hipSuccess ||
+                                                     64 * M16<D, G>::kWaves, 0) != hipSuccess ||
         nb < 1)
       nb = 1;
     return nb;
@@ -399,7 +415,9 @@ auto by_group16(int group, F&& f) {
 
 }  // namespace
 
-int gqa_mma16_tile(int group) { return group <= 16 ? 64 : (group == 32 ? 32 : 16); }
+int gqa_mma16_tile(int group) {
+  return by_group16(group, [](auto g) { return M16<128, decltype(g)::value>::kTP; });
+}
 
 int gqa_mma16_groups(int D, int group) {
   const int cus = m16_device_cus();
@@ -424,7 +442,7 @@ hipError_t launch_gqa_mma16(int D, int group, const GqaArgs& a, int groups, bool
   }
   auto f = [&](auto g) {
     constexpr int G = decltype(g)::value;
-    const dim3 grid((unsigned)groups), block(64 * kWaves);
+    const dim3 grid((unsigned)groups), block(64 * M16<128, G>::kWaves);
     if (D == 128) {
       if (split) hipLaunchKernelGGL((gqa_mma16_kernel<128, G, true>), grid, block, 0, s, a);
       else hipLaunchKernelGGL((gqa_mma16_kernel<128, G, false>), grid, block, 0, s, a);

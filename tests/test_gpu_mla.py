@@ -2,7 +2,8 @@
 
 Tolerances as for the GQA path: bf16 inputs, fp32 accumulation -> max-abs 2e-3
 for fp32-written results (partial kernel + merge in fp32), plus half a bf16
-ulp of the oracle value when the result itself is bf16. Bit-exact: one cached
+ulp of the oracle value when the result itself is bf16. Rows of one, a few
+and hundreds of partitions, and empty rows among full ones, are covered. Bit-exact: one cached
 position returns its latent, NaN padding is never read, repeated runs agree.
 """
 
@@ -51,6 +52,8 @@ CASES = [
     (2, 96, 200, [200, 150]),
     (1, 256, 130, [130]),
     (2, 128, 40, [5, 40]),
+    (4, 128, 4096, [4096, 700, 0, 2049]),     # 16 partitions of 256: rows of 16, 3, 0 and 9 of them
+    (1, 128, 65536, [65536]),                 # 256 partitions of one row, merged by the last
 ]
 
 

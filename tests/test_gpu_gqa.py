@@ -90,6 +90,8 @@ def test_gqa_matches_oracle(gpu, case, P):
         got = _f64(out)
         bound = tol + (_half_ulp_bf16(ref) if dt == torch.bfloat16 else 0.0)
         assert np.all(np.abs(got - ref) <= bound), float(np.abs(got - ref).max())
+        if dt == torch.bfloat16:  # the fp32 result rounded once to bf16
+            assert np.all(np.abs(got - ref) <= _half_ulp_bf16(ref) + 1e-5), float(np.abs(got - ref).max())
     else:
         got = _f64(_run_fp32_out(m, gq, gk, gv, gl, P, w.scale))
         err = float(np.abs(got - ref).max())
@@ -209,19 +211,22 @@ def _full_parity(w):
     got = _f64(out)
     del gq, gk, gv
     assert np.isfinite(got).all()
-    worst = 0.0
+    worst = excess = 0.0
     for b in range(w.B):
         ref = oracle.decode_gqa(q[b:b + 1], k[b:b + 1], v[b:b + 1], l[b:b + 1], w.scale)[0]
         err = np.abs(got[b] - ref)
         worst = max(worst, float(err.max()))
+        excess = max(excess, float((err - _half_ulp_bf16(ref)).max()))
         assert np.all(err <= 2e-3 + _half_ulp_bf16(ref)), (b, float(err.max()))
-    return worst
+        # the fp32-accumulated result rounded once to bf16: half a bf16 ulp plus 1e-5
+        assert np.all(err <= _half_ulp_bf16(ref) + 1e-5), (b, float((err - _half_ulp_bf16(ref)).max()))
+    return worst, excess
 
 
 @pytest.mark.parametrize("name", ["mha7b", "gqa4", "gqa8", "mqa"])
 def test_full_size_workload_every_row(gpu, name):
-    worst = _full_parity(W.NAMED[name])
-    print(f"{name}: worst max-abs error over all rows {worst:.3e}")
+    worst, excess = _full_parity(W.NAMED[name])
+    print(f"{name}: worst max-abs error over all rows {worst:.3e}; beyond the bf16 rounding {excess:.3e}")
 
 
 @pytest.mark.parametrize("B,h_q,h_kv,D", [(150, 8, 2, 64), (100, 64, 8, 128), (70, 16, 16, 128)])

@@ -68,6 +68,8 @@ def test_mla_matches_oracle(gpu, case, P):
     if P == 0:
         got = _f64(m.attn_decode_mla(gqn, gqr, glat, gl, w.scale))
         assert np.all(np.abs(got - ref) <= 2e-3 + _half_ulp_bf16(ref)), float(np.abs(got - ref).max())
+        # the fp32-accumulated result rounded once to bf16: half a bf16 ulp plus 1e-5
+        assert np.all(np.abs(got - ref) <= _half_ulp_bf16(ref) + 1e-5), float(np.abs(got - ref).max())
     else:
         got = _f64(_fp32_out(m, gqn, gqr, glat, gl, w.scale, P))
         err = float(np.abs(got - ref).max())
@@ -155,9 +157,12 @@ def test_full_size_workload_every_row(gpu):
     (qn, qr, lat, l), (gqn, gqr, glat, gl) = _inputs(w, gpu)
     got = _f64(m.attn_decode_mla(gqn, gqr, glat, gl, w.scale))
     assert np.isfinite(got).all()
-    worst = 0.0
+    worst = excess = 0.0
     for b in range(w.B):
         ref = oracle.decode_mla(qn[b:b + 1], qr[b:b + 1], lat[b:b + 1], l[b:b + 1], w.scale, w.d_c)[0]
-        worst = max(worst, float(np.abs(got[b] - ref).max()))
-        assert np.all(np.abs(got[b] - ref) <= 2e-3 + _half_ulp_bf16(ref)), b
-    print(f"mla full size: worst max-abs error over all rows {worst:.3e}")
+        err = np.abs(got[b] - ref)
+        worst = max(worst, float(err.max()))
+        excess = max(excess, float((err - _half_ulp_bf16(ref)).max()))
+        assert np.all(err <= 2e-3 + _half_ulp_bf16(ref)), b
+        assert np.all(err <= _half_ulp_bf16(ref) + 1e-5), b  # rounded once to bf16
+    print(f"mla full size: worst max-abs error over all rows {worst:.3e}; beyond the bf16 rounding {excess:.3e}")

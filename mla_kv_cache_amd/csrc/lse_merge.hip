@@ -80,12 +80,68 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void lse_merge_kernel(
   const int row = blockIdx.x * kRowsPerGroup + wave;  // b * H + h, uniform in the wave
   if (row >= rows) return;
   const int b = row / H;
-  const int n = attended_len(seq_lens[b], len_add, T_max);
-  const int span = n - window_lo(n, window);
-  const int npv = span / P + (span % P != 0);
   const float* lse = part_lse + (size_t)row * NP;
   const float* po = part_out + (size_t)row * NP * Dv;
   TO* o = out + (size_t)row * Dv;
+
+  // Up to four partitions and one or two 64 VW-wide slices per row (the MLA
+  // decode: four partitions of 512 values): every load of the row (its
+  // sequence length, the log-sum-exps, all partials, also of partitions past
+  // the row's valid ones) is issued at once, then the valid ones are combined
+  // in exactly the order of the general path below, so the bits are the same.
+  if (NP <= 4 && (Dv == 64 * VW || Dv == 128 * VW)) {
+    const int len = seq_lens[b];
+    const float lsv = lane < NP ? lse[lane] : kNegInf;
+    typename V::type x[2][4];
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        if (p < NP && sl * 64 * VW < Dv)
+          x[sl][p] = *reinterpret_cast<const typename V::type*>(po + (size_t)p * Dv + sl * 64 * VW + lane * VW);
+    const int n = attended_len(len, len_add, T_max);
+    const int span = n - window_lo(n, window);
+    const int npv = span / P + (span % P != 0);
+    float M = kNegInf;
+    if (lane < npv) M = fmaxf(M, lsv);
+    M = wave_max(M);
+    float W = 0.f;
+    if (lane < npv) W += fast_exp2(lsv - M);
+    const float invW = 1.f / wave_sum(W);
+    float wp[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) wp[p] = fast_exp2(__shfl(lsv, p, 64) - M) * invW;
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      if (sl * 64 * VW >= Dv) break;
+      float acc[4][VW];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < VW; ++i) acc[u][i] = 0.f;
+      if (npv == 4) {  // the general path's four-at-a-time step
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < VW; ++i) acc[u][i] = fmaf(wp[u], V::get(x[sl][u], i), acc[u][i]);
+      } else {         // its one-at-a-time tail
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          if (p < npv)
+#pragma unroll
+            for (int i = 0; i < VW; ++i) acc[0][i] = fmaf(wp[p], V::get(x[sl][p], i), acc[0][i]);
+      }
+      float r[VW];
+#pragma unroll
+      for (int i = 0; i < VW; ++i) r[i] = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+      store_out<VW>(o + sl * 64 * VW + lane * VW, r);
+    }
+    return;
+  }
+
+  const int n = attended_len(seq_lens[b], len_add, T_max);
+  const int span = n - window_lo(n, window);
+  const int npv = span / P + (span % P != 0);
 
   float M = kNegInf;
   for (int p = lane; p < npv; p += 64) M = fmaxf(M, lse[p]);

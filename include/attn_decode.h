@@ -52,15 +52,17 @@
  *   e.g. across devices); the one-call entry points run both with the
  *   library's own partition size and a caller-provided workspace.
  * - bf16 GQA (every supported g; contiguous caches, and paged caches whose
- *   pages hold at least 32 positions, 16 at g = 64) is split differently
+ *   pages hold at least 32 positions, 16 at g = 64, 64 at g in {3, 5, 6, 7})
+ *   is split differently
  *   by the one-call entry points: every resident work-group takes an equal
  *   share of all (sequence, KV head, 128-position unit) work, and each
  *   work-group's share of a (sequence, KV head) row is one partial. The cut
  *   points then depend on the sequence lengths and on the device's compute-
  *   unit count; on one device the output is still bit-identical from run to
- *   run. Which kernel runs is a function of (D, g, page size): g <= 4 streams
- *   one position per lane on the vector ALUs; g = 8 to 64 scores and sums on
- *   16x16 matrix-core tiles; g = 128 on 32x32 tiles (a paged cache picks
+ *   run. Which kernel runs is a function of (D, g, page size): g in {1, 2, 4}
+ *   streams one position per lane on the vector ALUs; g = 8 to 64, and g in
+ *   {3, 5, 6, 7}, scores and sums on 16x16 matrix-core tiles (the groups below
+ *   16 in masked head columns); g = 128 on 32x32 tiles (a paged cache picks
  *   among them by which tile its pages hold whole). fp32 caches, and bf16
  *   pages too small for any of those tiles, run on fixed partitions through
  *   a generic kernel.
@@ -129,8 +131,9 @@ uint64_t attn_mla_cache_bytes(uint64_t n_layers, uint64_t d_c, uint64_t d_r,
  * v_cache  [B, h_kv, T_max, D]   dtype dt
  * seq_lens int32 [B]
  * out      [B, h_q, D]           dtype dt
- * Supported: D in {64, 128}; g = h_q / h_kv a power of two up to 128 (MHA
- * g = 1; MQA h_kv = 1 with h_q up to 128; other g: ATTN_ERR_UNSUPPORTED); dt
+ * Supported: D in {64, 128}; g = h_q / h_kv any of 1 to 8, or a power of two
+ * up to 128 (MHA g = 1; MQA h_kv = 1 with h_q up to 128; other g:
+ * ATTN_ERR_UNSUPPORTED); dt
  * in {ATTN_F32, ATTN_BF16}. B, h_kv and h_kv * max(1, g / 16) at most 65535
  * (ATTN_ERR_INVALID_ARG otherwise). Any B >= 1, T_max >= 1 with
  * B*h_kv*T_max*D < 2^40; one (sequence, KV head) slab, T_max*D*sizeof(elem),
@@ -245,8 +248,8 @@ int attn_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_
  * clamped to it); entries past a sequence's last used page are never read,
  * and pages may be shared between sequences (read-only here). page_size: a
  * power of two >= 16; the bf16 split kernels need pages of at least 32 rows
- * (16 at g = 64); smaller pages go through the generic kernel's per-row
- * gather (slower). A used table entry outside
+ * (16 at g = 64, 64 at g in {3, 5, 6, 7}); smaller pages go through the
+ * generic kernel's per-row gather (slower). A used table entry outside
  * [0, num_pages) never faults: its rows read as zeros (or as a clamped page on
  * the per-row path) and the result for that sequence is unspecified.
  * Workspace: attn_decode_gqa_workspace_bytes(B, h_q, h_kv, D, T_max, dt). */

@@ -1053,7 +1053,11 @@ hipError_t launch_d(int G, const GqaArgs& a, hipStream_t s) {
   switch (G) {
     case 1: return launch_one<E, D, 1>(a, 1, s);
     case 2: return launch_one<E, D, 2>(a, 1, s);
+    case 3: return launch_one<E, D, 3>(a, 1, s);
     case 4: return launch_one<E, D, 4>(a, 1, s);
+    case 5: return launch_one<E, D, 5>(a, 1, s);
+    case 6: return launch_one<E, D, 6>(a, 1, s);
+    case 7: return launch_one<E, D, 7>(a, 1, s);
     case 8: return launch_one<E, D, 8>(a, 1, s);
     default:  // groups of 16 or more: chunks of 16 heads
       if (G % 16 != 0) return hipErrorInvalidValue;
@@ -1091,7 +1095,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const unsigned char* __r
 // for the 16 x 16 matrix-core kernel (groups of up to 16, 32, 64 heads), 32
 // rows for the position-per-lane and the 32 x 32 matrix-core kernels.
 BfKernel bf16_kernel(int D, int group, int page_size) {
-  if (!(D == 64 || D == 128) || !pow2(group)) return BfKernel::kGeneric;
+  if (!(D == 64 || D == 128) || !gqa_group_supported(group)) return BfKernel::kGeneric;
+  if (!pow2(group))  // groups of 3, 5, 6, 7: the 16 x 16 kernel's masked head columns
+    return page_size == 0 || page_size % gqa_mma16_tile(group) == 0 ? BfKernel::kMma16 : BfKernel::kGeneric;
   const bool fits32 = page_size == 0 || page_size % kPoRows == 0;
   if (group >= 8 && group <= 64 && (page_size == 0 || page_size % gqa_mma16_tile(group) == 0))
     return BfKernel::kMma16;

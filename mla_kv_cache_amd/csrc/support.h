@@ -7,10 +7,11 @@ namespace attn {
 inline bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 // dt: 0 = fp32 storage, 1 = bf16 storage (values of attn_dtype).
-// GQA / MHA / MQA: head dim 64 or 128, group size g = h_q / h_kv a power of
-// two up to 128 (h_kv = 1 with up to 128 query heads is MQA).
+// GQA / MHA / MQA: head dim 64 or 128, group size g = h_q / h_kv any of 1 to
+// 8 or a power of two up to 128 (h_kv = 1 with up to 128 query heads is MQA).
+inline bool gqa_group_supported(int group) { return (group >= 1 && group <= 8) || (pow2(group) && group <= 128); }
 inline bool gqa_supported(int dt, int D, int group) {
-  return (dt == 0 || dt == 1) && (D == 64 || D == 128) && pow2(group) && group <= 128;
+  return (dt == 0 || dt == 1) && (D == 64 || D == 128) && gqa_group_supported(group);
 }
 
 // The bf16 persistent position-per-lane kernel: groups of up to 8 heads.

@@ -134,7 +134,8 @@ def _gqa(lib, **kw):
     (dict(T=1 << 23, B=1, h_q=2, h_kv=1), UNSUPPORTED),   # one 2 GiB K slab: past 32-bit offsets
     (dict(T=(1 << 23) - 1, B=1, h_q=2, h_kv=1, wsb=0), WORKSPACE),
     (dict(D=96), UNSUPPORTED), (dict(D=256), UNSUPPORTED),
-    (dict(h_q=24, h_kv=1), UNSUPPORTED), (dict(h_q=12, h_kv=4), UNSUPPORTED),
+    (dict(h_q=24, h_kv=1), UNSUPPORTED), (dict(h_q=36, h_kv=4), UNSUPPORTED),   # groups of 24, 9
+    (dict(h_q=48, h_kv=4), UNSUPPORTED),              # groups of 12: not a power of two above 8
     (dict(h_q=512, h_kv=2), UNSUPPORTED),             # groups of 256: above the 128 built
     (dict(dt=7), UNSUPPORTED),
     (dict(q=ctypes.c_void_p((1 << 20) + 8)), UNSUPPORTED),
@@ -144,6 +145,15 @@ def _gqa(lib, **kw):
 ])
 def test_gqa_argument_checks(lib, kw, expect):
     assert _gqa(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(12, 4), (10, 2), (12, 2), (28, 4), (40, 8)])
+def test_gqa_groups_of_three_to_seven_are_planned(lib, h_q, h_kv):
+    """Every group size from 1 to 8 is built (here 3, 5, 6, 7, 5): the plan succeeds."""
+    ws = ctypes.c_size_t(0)
+    for dt in (0, BF16):
+        assert lib.attn_decode_gqa_plan(2, h_q, h_kv, 128, 1024, dt, None, None, ctypes.byref(ws)) == OK
+        assert ws.value > 0
 
 
 def test_gqa_partial_and_merge_checks(lib):

@@ -73,6 +73,13 @@ CASES = [
     (2, 32, 2, 128, 800, torch.bfloat16, [800, 799]),
     (2, 32, 1, 64, 500, torch.float32, [500, 77]),
     (1, 128, 1, 128, 300, torch.float32, [300]),
+    # groups that are not powers of two (3, 5, 6, 7: the 16 x 16 kernel's masked head
+    # columns for bf16, the generic kernel for fp32)
+    (2, 12, 4, 128, 900, torch.bfloat16, [900, 333]),
+    (2, 10, 2, 64, 500, torch.bfloat16, [500, 129]),
+    (3, 28, 4, 128, 700, torch.bfloat16, [700, 1, 64]),
+    (2, 12, 2, 128, 600, torch.float32, [600, 77]),
+    (2, 21, 3, 64, 300, torch.float32, [300, 10]),
 ]
 
 
@@ -109,7 +116,8 @@ def test_tiny_fp32_workload(gpu):
     assert float(np.abs(_f64(out) - ref).max()) <= 1e-5
 
 
-@pytest.mark.parametrize("h_q,h_kv,D", [(16, 4, 128), (32, 1, 128), (128, 1, 128), (64, 2, 64), (32, 2, 128)])
+@pytest.mark.parametrize("h_q,h_kv,D", [(16, 4, 128), (32, 1, 128), (128, 1, 128), (64, 2, 64), (32, 2, 128),
+                                         (12, 4, 128), (28, 4, 64)])
 def test_single_position_is_bit_exact(gpu, h_q, h_kv, D):
     m = _m()
     g = h_q // h_kv

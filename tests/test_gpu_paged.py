@@ -58,12 +58,14 @@ def _paginate_kv(cache, lens, page_size, seed, spare=3):
 
 def _kernel(dt, D, g, ps):
     """Which kernel serves a shape (page size 0: contiguous), as the library's header states it:
-    bf16 groups of 8 to 64 on 16 x 16 matrix-core tiles of 64 or 16 positions (groups up to 32,
-    groups of 64), groups up to 8 position-per-lane and groups of 16 to 128 on 32 x 32 tiles (pages
-    of 32 rows), anything else per row."""
+    bf16 groups of 8 to 64, and of 3, 5, 6, 7, on 16 x 16 matrix-core tiles of 64 or 16 positions
+    (groups up to 32, groups of 64), power-of-two groups up to 8 position-per-lane and groups of 16
+    to 128 on 32 x 32 tiles (pages of 32 rows), anything else per row."""
     if dt == torch.float32:
         return "generic"
     tile16 = 64 if g <= 32 else 16
+    if g & (g - 1):  # not a power of two
+        return "mma16" if ps == 0 or ps % tile16 == 0 else "generic"
     if 8 <= g <= 64 and (ps == 0 or ps % tile16 == 0):
         return "mma16"
     if g <= 8 and ps % 32 == 0:
@@ -86,6 +88,8 @@ CASES = [
     (3, 32, 4, 64, 24, 32, torch.bfloat16, [700, 33, 768]),
     (3, 32, 1, 128, 16, 64, torch.bfloat16, [1024, 100, 1]),     # MQA, matrix cores
     (2, 64, 2, 128, 20, 32, torch.bfloat16, [640, 45]),          # groups of 32 in 32-row pages: 32 x 32 tiles
+    (2, 12, 4, 128, 16, 64, torch.bfloat16, [1000, 100]),        # groups of 3: 16 x 16 tiles
+    (2, 28, 4, 128, 32, 32, torch.bfloat16, [900, 31]),          # groups of 7 in 32-row pages: per-row gather
     (2, 128, 2, 64, 8, 32, torch.bfloat16, [256, 77]),
     (2, 64, 1, 128, 32, 16, torch.bfloat16, [500, 17]),          # 16-row pages: chunks of 16 heads
     (2, 32, 1, 64, 10, 32, torch.float32, [300, 12]),

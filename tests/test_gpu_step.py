@@ -55,6 +55,7 @@ GQA_CASES = [
     (2, 16, 1, 128, 900, torch.bfloat16, [63, 511]),
     (2, 32, 2, 128, 777, torch.bfloat16, [776, 100]),
     (3, 32, 1, 128, 900, torch.bfloat16, [899, 128, 0]),     # MQA, matrix cores
+    (2, 28, 4, 128, 700, torch.bfloat16, [699, 0]),          # groups of 7
     (2, 128, 2, 64, 500, torch.bfloat16, [255, 499]),
     (2, 32, 1, 64, 300, torch.float32, [299, 31]),
     (2, 8, 8, 64, 300, torch.float32, [299, 0]),

@@ -34,6 +34,7 @@ def _half_ulp_bf16(x):
 CASES = [
     # (B, h_q, h_kv, D, T_max, dtype, lens, window)
     (3, 8, 2, 128, 1000, torch.bfloat16, [1000, 517, 3], 100),
+    (2, 28, 4, 128, 1500, torch.bfloat16, [1500, 300], 512),   # groups of 7
     (2, 32, 32, 128, 2100, torch.bfloat16, [2100, 1500], 700),
     (2, 16, 2, 128, 3000, torch.bfloat16, [3000, 64], 1),
     (2, 64, 8, 128, 5000, torch.bfloat16, [5000, 4097], 4096),

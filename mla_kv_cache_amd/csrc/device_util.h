@@ -94,36 +94,21 @@ __device__ __forceinline__ float wave_sum(float x) {
   return xor32_sum(xor16_sum(x));
 }
 
-// Issue one 16-byte-per-lane copy from global memory straight into LDS
-// (global_load_lds_dwordx4): lane i's 16 bytes land at lds_base + 16*i.
-// lds_base must be wave-uniform. Written as inline assembly so that the
-// compiler does not wait for the copy before unrelated LDS reads; the caller
-// waits with s_waitcnt vmcnt. The instruction writes no register, only LDS;
-// M0 carries the LDS address and no other code in these kernels uses M0.
-// M0 is a reserved register to the compiler, which warns when an assembly
-// block names it as clobbered; the clobber is kept so that the compiler never
-// assumes a value of its own survives the block.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void copy16_to_lds(uint32_t lds_base, const void* src) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(src) : "memory", "m0");
-}
+// Cache policy of the cache streams (K and V rows, latent rows, projection
+// weights): non-temporal. Every byte of a stream is read once per call, so
+// nothing is gained by keeping it in the L2 or the last-level cache. A plain
+// read of 1 GiB on MI355X streams at 6.0-6.4 TB/s with the default policy and
+// at 6.7-7.1 TB/s with this one; the decode kernels run 10-13% faster with it,
+// with unchanged results. In inline assembly the policy is the `nt` modifier;
+// in the buffer load builtins it is this cache-policy operand.
+constexpr int kLoadNonTemporal = 2;
 
-// Same copy with a wave-uniform base address (scalar register pair) and a
-// per-lane 32-bit byte offset: one VGPR per lane instead of a 64-bit address.
-__device__ __forceinline__ void copy16_to_lds_sbase(uint32_t lds_base, const void* sbase, uint32_t voff) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
-  // readfirstlane returns a signed int: widen each half through uint32_t so
-  // the low half is zero-extended (a sign-extended low half would corrupt the
-  // upper 32 address bits whenever its bit 31 is set).
-  const uint64_t sb = (uint64_t)(uintptr_t)sbase;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32));
-  const uint64_t sbu = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(base), "v"(voff), "s"(sbu) : "memory", "m0");
+// 16-byte vector load with the non-temporal policy.
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
-#pragma clang diagnostic pop
 
 // 16-byte vector store. Every call site guarantees 16-byte alignment.
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }

@@ -162,9 +162,9 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_kernel(const GqaArgs a) 
 #pragma unroll
     for (int i = 0; i < NI; ++i) ro[i] = row_off(r0 + i * RPI + rr);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kr[i] = ld16(kb + ro[i]);
+    for (int i = 0; i < NI; ++i) kr[i] = ld16_nt(kb + ro[i]);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) vr[i] = ld16(vb + ro[i]);
+    for (int i = 0; i < NI; ++i) vr[i] = ld16_nt(vb + ro[i]);
 
     float s[NI][G];
 #pragma unroll
@@ -659,6 +659,7 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
   // K tile -> LDS buffer. Copy i moves rows RPC*i .. RPC*i + RPC - 1 of the
   // tile (one KiB); its lane l fills LDS chunk 64*i + l, i.e. row RPC*i + l / CH,
   // stored chunk l % CH, which carries logical chunk (l % CH) ^ (row % CH).
+  // K and V loads use the non-temporal cache policy (every row is read once).
   constexpr int RPC = 1024 / (D * 2);           // rows per copy
   constexpr int KPER = (RPC % CH == 0) ? 1 : CH / RPC;
   uint32_t kvoff[KPER];
@@ -677,7 +678,7 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       const uint32_t soff = tile_off + 1024u * i;
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
                    ::"s"(dst + 1024u * i), "v"(kvoff[i % KPER]), "s"(kr), "s"(soff)
                    : "memory", "m0");
     }
@@ -686,7 +687,7 @@ __global__ __launch_bounds__(kThreads) void gqa_partial_po_kernel(const GqaArgs 
   // V rows -> registers (row layout): load i brings rows i*RPI .. i*RPI+RPI-1.
   const uint32_t vvoff = (uint32_t)(rr * D + c * 8) * 2u;
   auto load_v = [&](const __amdgpu_buffer_rsrc_t& vr_, uint32_t tile_off, int i) {
-    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(vr_, vvoff, tile_off + 1024u * i, 0);
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(vr_, vvoff, tile_off + 1024u * i, kLoadNonTemporal);
     return make_uint4(w.x, w.y, w.z, w.w);
   };
 

@@ -175,7 +175,8 @@ __global__ __launch_bounds__((64 * MxCfg<D, G>::kWaves)) void gqa_matrix_kernel(
 
   // The copies of one tile into a buffer: kPerWave 1 KiB blocks per wave,
   // buffer_load_dwordx4 ... lds (M0 holds the LDS address; the compiler is
-  // told M0 is clobbered, and it uses M0 for nothing else here).
+  // told M0 is clobbered, and it uses M0 for nothing else here), with the
+  // non-temporal cache policy (`nt`: every row is read once per call).
   auto issue_tile = [&](unsigned char* buf, const items::Cursor& c) {
     __amdgpu_buffer_rsrc_t kr, vr;
     uint32_t soff;
@@ -187,7 +188,7 @@ __global__ __launch_bounds__((64 * MxCfg<D, G>::kWaves)) void gqa_matrix_kernel(
       const __amdgpu_buffer_rsrc_t rs = m < C::kPerWave / 2 ? kr : vr;
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
                    ::"s"(dst), "v"(voff[m]), "s"(rs), "s"(soff) : "memory", "m0");
 #pragma clang diagnostic pop
     }

@@ -171,6 +171,8 @@ __global__ __launch_bounds__((64 * M16<D, G>::kWaves)) void gqa_mma16_kernel(con
     soff = 0;
   };
 
+  // The copies of one tile into a buffer, with the non-temporal cache policy
+  // (`nt`: every row is read once per call).
   auto issue_tile = [&](unsigned char* buf, const items::Cursor& c) {
     __amdgpu_buffer_rsrc_t kr, vr;
     uint32_t soff;
@@ -182,7 +184,7 @@ __global__ __launch_bounds__((64 * M16<D, G>::kWaves)) void gqa_mma16_kernel(con
       const __amdgpu_buffer_rsrc_t rs = visv[m] ? vr : kr;
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
                    ::"s"(dst), "v"(voff[m]), "s"(rs), "s"(soff) : "memory", "m0");
 #pragma clang diagnostic pop
     }

@@ -112,7 +112,8 @@ struct TileCopy {
 // chunk's byte offset within the tile (tile_voffsets). Rows at or past the
 // resource's num_records bytes arrive as zeros.
 //
-// The copy is issued as buffer_load_dwordx4 ... lds in inline assembly: it
+// The copy uses the non-temporal cache policy (`nt`: every latent row is read
+// once per call) and is issued as buffer_load_dwordx4 ... lds in inline assembly: it
 // writes no register, only LDS, and M0 holds the block's LDS address (no
 // other code in these kernels uses M0). Written this way the compiler does not
 // insert a wait for the copy before every later LDS read (it cannot prove that
@@ -128,7 +129,7 @@ __device__ __forceinline__ void copy_block(unsigned char* buf, __amdgpu_buffer_r
                                            uint32_t voff, int wave, int k) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)buf;
   const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + 1024u * (uint32_t)(wave + NWAVES * k));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
                ::"s"(dst), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 #pragma clang diagnostic pop

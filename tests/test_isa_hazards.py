@@ -155,7 +155,7 @@ def _m0_violations(lines: list[str]) -> list[str]:
     return bad
 
 
-@pytest.mark.parametrize("name", ["gqa_decode.hip", "mla_decode.hip", "lse_merge.hip", "mla_absorb.hip"])
+@pytest.mark.parametrize("name", ["gqa_decode.hip", "gqa_mma16.hip", "gqa_matrix.hip", "mla_decode.hip", "lse_merge.hip", "mla_absorb.hip"])
 def test_m0_is_only_used_by_the_copy_blocks(name, tmp_path):
     lines = _assembly(os.path.join(CSRC, name), tmp_path)
     bad = _m0_violations(lines)

@@ -1,4 +1,5 @@
-"""Wait-state rules around the hand-scheduled assembly blocks, and the use of M0 (CPU only).
+"""Wait-state rules around the hand-scheduled assembly blocks, the use of M0, and the cache
+policy of the cache streams (CPU only).
 
 The GQA kernel issues some DPP arithmetic as inline assembly. The compiler
 inserts the wait states gfx950 needs between dependent instructions of the
@@ -205,3 +206,21 @@ def test_scanner_catches_planted_hazards():
     ]
     bad = _violations(lines)
     assert len(bad) == 3, bad
+
+
+# Cache policy of the cache streams: every K, V and latent copy (the
+# direct-to-LDS copies and the V register loads) carries the non-temporal
+# policy, which the decode kernels' streaming rate depends on. The scan
+# counts, per kernel source, the copies that carry `nt` and fails on any
+# that does not.
+@pytest.mark.parametrize("name,min_copies", [("gqa_decode.hip", 2), ("gqa_mma16.hip", 1), ("gqa_matrix.hip", 1),
+                                             ("mla_decode.hip", 1)])
+def test_cache_streams_are_non_temporal(name, min_copies, tmp_path):
+    lines = _assembly(os.path.join(CSRC, name), tmp_path)
+    copies = [t for t in lines if _is_instr(t) and _is_lds_copy(t)]
+    assert len(copies) >= min_copies, name
+    plain = [t for t in copies if " nt" not in t]
+    assert not plain, plain[:4]
+    if name == "gqa_decode.hip":  # the V rows of the position-per-lane kernel go to registers
+        vloads = [t for t in lines if t.startswith("buffer_load_dwordx4 v[") and "offen" in t]
+        assert vloads and all(" nt" in t for t in vloads), [t for t in vloads if " nt" not in t][:4]

@@ -31,10 +31,12 @@ copy, and that no instruction that reads M0 implicitly appears elsewhere.
 
 from __future__ import annotations
 
+import functools
 import os
 import re
 import shutil
 import subprocess
+import tempfile
 
 import pytest
 
@@ -45,13 +47,21 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
 
 
-def _assembly(src: str, tmp_path) -> list[str]:
-    out = tmp_path / (os.path.basename(src) + ".s")
-    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", str(out), src]
-    subprocess.run(cmd, check=True, capture_output=True)
-    return [ln.split(";")[0].strip() for ln in out.read_text().splitlines()]
+@functools.lru_cache(maxsize=None)
+def _assembly_of(src: str) -> tuple[str, ...]:
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, os.path.basename(src) + ".s")
+        cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
+               "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", out, src]
+        subprocess.run(cmd, check=True, capture_output=True)
+        with open(out) as f:
+            return tuple(ln.split(";")[0].strip() for ln in f.read().splitlines())
+
+
+def _assembly(src: str, tmp_path=None) -> list[str]:
+    """The gfx950 assembly of one source, compiled once per test session."""
+    return list(_assembly_of(src))
 
 
 def _vregs(tok: str) -> set[str]:

@@ -55,6 +55,9 @@ __device__ __forceinline__ void store_tile(uint16_t* __restrict__ out, const f32
 // padded by 16 bytes so that the 16-byte fragment reads of 16 consecutive
 // rows fall on 64 distinct banks.
 constexpr int kAqPitch = 16 * kChunk * 2 + 16;
+// 16-byte query pieces each thread stages per chunk
+constexpr int kAqStage = 32 * kMTilesPerPass * 2 * kChunk / (64 * kWavesPerGroup);
+static_assert(kAqStage * 64 * kWavesPerGroup == 32 * kMTilesPerPass * 2 * kChunk, "whole pieces per thread");
 
 // One wave per 32 latent columns c of one head; all of B in passes of
 // kMTilesPerPass tiles of 32 rows. The four waves of a work-group share the
@@ -86,12 +89,22 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void absorb_q_kernel(
         const int k0 = kb + 16 * i;
         bw[i] = (active && k0 < d_h) ? ld16(wrow + k0) : make_uint4(0, 0, 0, 0);
       }
-      if (staged) __syncthreads();  // the previous chunk's reads are done
-      for (int i = threadIdx.x; i < 32 * kMTilesPerPass * 2 * kChunk; i += blockDim.x) {
+      // this thread's query pieces: every load issued before the first store
+      // (one memory round trip, not one per piece)
+      uint4 qv[kAqStage];
+#pragma unroll
+      for (int it = 0; it < kAqStage; ++it) {
+        const int i = threadIdx.x + it * 64 * kWavesPerGroup;
         const int r = i / (2 * kChunk), c = i % (2 * kChunk);
         const int m = mt0 * 32 + r, k = kb + 8 * c;
-        *reinterpret_cast<uint4*>(qs + r * kAqPitch + 16 * c) =
-            (m < B && k < d_h) ? ld16(q + ((size_t)m * H + h) * d_h + k) : make_uint4(0, 0, 0, 0);
+        qv[it] = (m < B && k < d_h) ? ld16(q + ((size_t)m * H + h) * d_h + k) : make_uint4(0, 0, 0, 0);
+      }
+      if (staged) __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+      for (int it = 0; it < kAqStage; ++it) {
+        const int i = threadIdx.x + it * 64 * kWavesPerGroup;
+        const int r = i / (2 * kChunk), c = i % (2 * kChunk);
+        *reinterpret_cast<uint4*>(qs + r * kAqPitch + 16 * c) = qv[it];
       }
       __syncthreads();
       staged = true;
@@ -122,6 +135,9 @@ constexpr int kUpCols = 32 * kUpColW;           // W_UV columns per work-group (
 constexpr int kUpPitch = kUpCols * 2 + 32;      // bytes per LDS row: padding spreads the transposed reads
 constexpr int kUpMaxRows = 512;                 // the whole contraction of one head fits in LDS
 constexpr int kUpPartSteps = kUpMaxRows / 16 / kUpKSplit;  // 16-row k-steps of a wave's part (at most)
+// 16-byte W_UV pieces each thread stages per piece of the contraction (at most)
+constexpr int kUpStage = kUpMaxRows * (kUpCols / 8) / (64 * kUpWaves);
+static_assert(kUpStage * 64 * kUpWaves == kUpMaxRows * (kUpCols / 8), "whole pieces per thread");
 
 // One work-group per (head, 64 output columns); wave w takes the 32 columns
 // of half w % 2 and part w / 2 of the contraction. The head's W_UV slice
@@ -173,11 +189,25 @@ __global__ __launch_bounds__(64 * kUpWaves) void up_v_kernel(
                                                     : make_uint4(0, 0, 0, 0);
         }
       }
-      if (mt0 > 0 || kc > 0) __syncthreads();       // the previous piece's reads are done
-      if (mt0 == 0 || d_c > kUpMaxRows) {
-        for (int i = threadIdx.x; i < rows * (cols / 8); i += blockDim.x) {
+      const bool stage = mt0 == 0 || d_c > kUpMaxRows;
+      // this thread's W_UV pieces: every load issued before the first store
+      // (one memory round trip, not one per piece)
+      uint4 wv[kUpStage];
+      if (stage) {
+#pragma unroll
+        for (int it = 0; it < kUpStage; ++it) {
+          const int i = threadIdx.x + it * 64 * kUpWaves;
           const int r = i / (cols / 8), c8 = i % (cols / 8);
-          *reinterpret_cast<uint4*>(wt + r * kUpPitch + c8 * 16) = ld16(wsrc + (size_t)(kc + r) * d_v + c8 * 8);
+          wv[it] = i < rows * (cols / 8) ? ld16(wsrc + (size_t)(kc + r) * d_v + c8 * 8) : make_uint4(0, 0, 0, 0);
+        }
+      }
+      if (mt0 > 0 || kc > 0) __syncthreads();       // the previous piece's reads are done
+      if (stage) {
+#pragma unroll
+        for (int it = 0; it < kUpStage; ++it) {
+          const int i = threadIdx.x + it * 64 * kUpWaves;
+          const int r = i / (cols / 8), c8 = i % (cols / 8);
+          if (i < rows * (cols / 8)) *reinterpret_cast<uint4*>(wt + r * kUpPitch + c8 * 16) = wv[it];
         }
         __syncthreads();
       }

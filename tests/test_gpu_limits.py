@@ -6,6 +6,9 @@
   two slabs per cache (the second starts past 4 GiB of the tensor) or two
   sequences (MLA), against the fp64 oracle on the full rows.
 * Most sequences: B = 65535, the host's limit, with short ragged rows.
+* Page pools past 4 GiB: every used page lies beyond the first 4 GiB of its
+  pool (page offsets are 64-bit), the rest of the pool is zeros; the paged
+  decode must give the contiguous decode's bits and match the oracle.
 
 The scores of long rows are made peaked (the query scaled by 4, exact in
 bf16) so that each output is carried by a few rows and a misread row changes
@@ -145,3 +148,60 @@ def test_most_mla_sequences(gpu):
     _assert_bf16_close(out, ref, "mla")
     empty = (lens == 0).nonzero().flatten().to(gpu)
     assert torch.equal(out[empty], torch.zeros_like(out[empty]))
+
+
+def _bits(t):
+    return t.detach().cpu().contiguous().view(torch.int16)
+
+
+def _high_pages(cache, lens, page_size, num_pages, gpu):
+    """Scatter the used pages of cache [B, heads, T, row] to the top of a zero pool of num_pages
+    pages (every 37th slot from the last down); returns (CPU pool, GPU pool, table)."""
+    B, H, T, R = cache.shape
+    npg = T // page_size
+    used = [(b, i) for b in range(B) for i in range(npg) if i * page_size < lens[b]]
+    pool = torch.zeros((num_pages, H, page_size, R), dtype=cache.dtype)
+    gpool = torch.zeros((num_pages, H, page_size, R), dtype=cache.dtype, device=gpu)
+    table = torch.full((B, npg), 1 << 30, dtype=torch.int32)   # past the last page: never read
+    for k, (b, i) in enumerate(used):
+        slot = num_pages - 1 - 37 * k
+        pool[slot] = cache[b, :, i * page_size:(i + 1) * page_size]
+        gpool[slot] = pool[slot].to(gpu)
+        table[b, i] = slot
+    return pool, gpool, table
+
+
+def test_paged_pools_past_4gib(gpu):
+    m = _m()
+    ps, lens = 64, [1024, 517, 1000]
+    w = W.small_gqa(3, 64, 8, 128, 1024, seed=77)
+    q, k, v, l = W.gqa_inputs(w, seq_lens=lens)
+    num_pages = 36000                                  # 128 KiB pages: 4.4 GiB per pool
+    kp, gkp, table = _high_pages(k, lens, ps, num_pages, gpu)
+    vp, gvp, _ = _high_pages(v, lens, ps, num_pages, gpu)
+    assert int(table[table < (1 << 30)].min()) * kp[0].numel() * 2 > 2 ** 32
+    gt, gl, gk, gv = table.to(gpu), l.to(gpu), k.to(gpu), v.to(gpu)
+    for g in (8, 4):                                   # 16x16 matrix-core and position-per-lane kernels
+        qs = q.view(3, 8, 8, 128)[:, :, :g].reshape(3, 8 * g, 128).contiguous()
+        gq = qs.to(gpu)
+        out = m.attn_decode_gqa_paged(gq, gkp, gvp, gt, gl, scale=w.scale)
+        lin = m.attn_decode_gqa(gq, gk, gv, gl, scale=w.scale)
+        assert torch.equal(_bits(out), _bits(lin)), g
+        ref = oracle.decode_gqa_paged(qs, kp, vp, table, l, w.scale, ps)
+        _assert_bf16_close(out, ref, g)
+    del kp, gkp, vp, gvp
+    torch.cuda.synchronize()
+
+    lens = [1024, 700]
+    wm = W.small_mla(2, 128, 1024, seed=78)
+    qn, qr, lat, l = W.mla_inputs(wm, seq_lens=lens)
+    num_pages = 62000                                  # 72 KiB pages: 4.3 GiB
+    lp, glp, table = _high_pages(lat[:, None], lens, ps, num_pages, gpu)
+    lp, glp = lp[:, 0], glp[:, 0]
+    assert int(table[table < (1 << 30)].min()) * lp[0].numel() * 2 > 2 ** 32
+    gqn, gqr, gl = qn.to(gpu), qr.to(gpu), l.to(gpu)
+    out = m.attn_decode_mla_paged(gqn, gqr, glp, table.to(gpu), gl, wm.scale)
+    lin = m.attn_decode_mla(gqn, gqr, lat.to(gpu), gl, wm.scale)
+    assert torch.equal(_bits(out), _bits(lin))
+    ref = oracle.decode_mla_paged(qn, qr, lp, table, l, wm.scale, wm.d_c, ps)
+    _assert_bf16_close(out, ref, "mla")

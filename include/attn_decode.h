@@ -298,8 +298,9 @@ int attn_decode_merge(const float* part_out, const float* part_lse, const int32_
  * 128 (MFMA tiles of 32 heads, one work-group per block of up to 128 heads);
  * bf16 only; one sequence's rows, T_max * (d_c + d_r) * 2 bytes, below 2 GiB
  * (ATTN_ERR_UNSUPPORTED otherwise: the kernels address them with 32-bit
- * offsets). The rotary key is used as stored: rotating it and q_rope by
- * position is the caller's job.
+ * offsets); B * H below 2^31 rows (ATTN_ERR_INVALID_ARG otherwise). The
+ * rotary key is used as stored: rotating it and q_rope by position is the
+ * caller's job.
  */
 int attn_decode_mla_plan(int B, int H, int d_c, int d_r, int T_max,
                          int* partition_size, int* num_partitions, size_t* workspace_bytes);

@@ -108,6 +108,8 @@ int check_mla_shape(const MlaShape& s) {
   if (s.B < 1 || s.H < 1 || s.d_c < 1 || s.d_r < 0 || s.T_max < 1) return ATTN_ERR_INVALID_ARG;
   if (s.T_max > kMaxTmax || s.B > kMaxGridYZ) return ATTN_ERR_INVALID_ARG;
   if (int64_t(s.B) * s.T_max * (s.d_c + s.d_r) >= kMaxElems) return ATTN_ERR_INVALID_ARG;
+  // Rows (b, h) are numbered with 32-bit integers (the merge).
+  if (int64_t(s.B) * s.H >= (int64_t(1) << 31)) return ATTN_ERR_INVALID_ARG;
   if (!attn::mla_supported(s.H, s.d_c, s.d_r)) return ATTN_ERR_UNSUPPORTED;
   // The kernels address one sequence's rows of a contiguous cache with 32-bit
   // byte offsets.

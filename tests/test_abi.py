@@ -186,6 +186,9 @@ def test_mla_argument_checks(lib):
     assert call(dc=256) == UNSUPPORTED
     assert call(H=48) == UNSUPPORTED
     assert call(scale=float("nan")) == INVALID
+    assert call(B=65535, H=32896, T=1) == INVALID     # 2^31 rows (b, h) or more
+    assert lib.attn_decode_mla_plan(65535, 32896, 512, 64, 1, None, None, None) == INVALID
+    assert lib.attn_decode_mla_plan(65535, 32768, 512, 64, 1, None, None, None) == OK
     assert call(wsb=64) == WORKSPACE
     assert call(out=P16c) == INVALID                  # output overlaps the latent cache
     assert call(lat=ctypes.c_void_p((1 << 34) + 4)) == UNSUPPORTED

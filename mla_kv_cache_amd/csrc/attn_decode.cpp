@@ -304,7 +304,7 @@ int attn_decode_merge(const float* part_out, const float* part_lse, const int32_
       overlap(out, out_b, part_lse, rows * NP * sizeof(float)))
     return ATTN_ERR_INVALID_ARG;
   if (attn::launch_merge(int(out_dt), part_out, part_lse, seq_lens, 0, 0, B, H, Dv, T_max,
-                         partition_size, NP, 0, out, stream) != hipSuccess)
+                         partition_size, NP, out, stream) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -390,7 +390,7 @@ int gqa_decode_impl(const void* q, const void* k_new, const void* v_new, const v
   }
   if (attn::launch_gqa_partial(int(dt), D, h_q / h_kv, a, stream) != hipSuccess) return ATTN_ERR_HIP;
   if (attn::launch_merge(int(dt), part_out, part_lse, seq_lens, k_new ? 1 : 0, window, B, h_q, D,
-                         T_max, P, NP, 0, out, stream) != hipSuccess)
+                         T_max, P, NP, out, stream) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -613,7 +613,7 @@ int mla_decode_impl(const void* q_nope, const void* q_rope, const void* lat_new,
                         float(double(scale) * kLog2e), part_out, part_lse};
   if (attn::launch_mla_partial(a, stream) != hipSuccess) return ATTN_ERR_HIP;
   if (attn::launch_merge(int(ATTN_BF16), part_out, part_lse, seq_lens, lat_new ? 1 : 0, 0, B, H,
-                         d_c, T_max, P, NP, attn::mla_xcd_group(B, H, NP), out, stream) != hipSuccess)
+                         d_c, T_max, P, NP, out, stream) != hipSuccess)
     return ATTN_ERR_HIP;
   return ATTN_OK;
 }

@@ -81,13 +81,9 @@ hipError_t launch_kv_append(int dt, const void* k_new, const void* v_new, void* 
 // len_add = 1 for a decode step: each row attends over min(max(seq_lens[b], 0) + 1, T_max)
 // positions instead of min(max(seq_lens[b], 0), T_max). window > 0: only the last
 // `window` of those positions, partitioned from the first of them.
-// xcd_group > 0: the partial kernel placed the partitions of each group of
-// xcd_group consecutive rows (g = row / xcd_group) on XCD g % 8; the merge then
-// reads them on that XCD. Ignored unless the rows divide into groups evenly
-// over the 8 XCDs.
 hipError_t launch_merge(int out_dt, const float* part_out, const float* part_lse,
                         const int32_t* seq_lens, int len_add, int window, int B, int H, int Dv,
-                        int T_max, int P, int NP, int xcd_group, void* out, hipStream_t stream);
+                        int T_max, int P, int NP, void* out, hipStream_t stream);
 
 struct MlaArgs {
   const void* q_nope;         // [B, H, 512]

@@ -12,10 +12,7 @@
 // walked eight (then four) at a time with independent loads so that several
 // partials of a lane are in flight together. M and the normaliser come from a wave-wide
 // pass over the log-sum-exps; each partition's weight is then recomputed
-// from its (wave-uniform) log-sum-exp where it is used. Work-groups go to the
-// 8 XCDs in turn (block index mod 8); when the partial kernel wrote each group
-// of rows from one XCD (the MLA decode), the merge takes a group's rows on
-// that XCD, whose L2 still holds part of the partials.
+// from its (wave-uniform) log-sum-exp where it is used.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -76,16 +73,11 @@ template <typename TO, int VW>
 __global__ __launch_bounds__(64 * kRowsPerGroup) void lse_merge_kernel(
     const float* __restrict__ part_out, const float* __restrict__ part_lse,
     const int32_t* __restrict__ seq_lens, int len_add, int window, int rows, int H, int Dv,
-    int T_max, int P, int NP, int xcd_group, TO* __restrict__ out) {
+    int T_max, int P, int NP, TO* __restrict__ out) {
   using V = Vec<VW>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int rb = blockIdx.x;
-  if (xcd_group > 0) {  // the rows of group g are merged on XCD g % 8, where their partials were written
-    const int per = xcd_group / kRowsPerGroup, x = blockIdx.x % 8, k = blockIdx.x / 8;
-    rb = ((k / per) * 8 + x) * per + k % per;
-  }
-  const int row = rb * kRowsPerGroup + wave;  // b * H + h, uniform in the wave
+  const int row = blockIdx.x * kRowsPerGroup + wave;  // b * H + h, uniform in the wave
   if (row >= rows) return;
   const int b = row / H;
   const float* lse = part_lse + (size_t)row * NP;
@@ -207,20 +199,19 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void lse_merge_kernel(
 template <typename TO>
 hipError_t launch_typed(const float* part_out, const float* part_lse, const int32_t* seq_lens,
                         int len_add, int window, int B, int H, int Dv, int T_max, int P, int NP,
-                        int xcd_group, TO* out, hipStream_t stream) {
+                        TO* out, hipStream_t stream) {
   const int rows = B * H;
-  if (xcd_group > 0 && (xcd_group % kRowsPerGroup != 0 || rows % (8 * xcd_group) != 0)) xcd_group = 0;
   const dim3 grid((unsigned)((rows + kRowsPerGroup - 1) / kRowsPerGroup));
   const dim3 block(64 * kRowsPerGroup);
   if (Dv % 256 == 0)
     hipLaunchKernelGGL((lse_merge_kernel<TO, 4>), grid, block, 0, stream, part_out, part_lse,
-                       seq_lens, len_add, window, rows, H, Dv, T_max, P, NP, xcd_group, out);
+                       seq_lens, len_add, window, rows, H, Dv, T_max, P, NP, out);
   else if (Dv % 128 == 0)
     hipLaunchKernelGGL((lse_merge_kernel<TO, 2>), grid, block, 0, stream, part_out, part_lse,
-                       seq_lens, len_add, window, rows, H, Dv, T_max, P, NP, xcd_group, out);
+                       seq_lens, len_add, window, rows, H, Dv, T_max, P, NP, out);
   else
     hipLaunchKernelGGL((lse_merge_kernel<TO, 1>), grid, block, 0, stream, part_out, part_lse,
-                       seq_lens, len_add, window, rows, H, Dv, T_max, P, NP, xcd_group, out);
+                       seq_lens, len_add, window, rows, H, Dv, T_max, P, NP, out);
   return hipGetLastError();
 }
 
@@ -401,11 +392,11 @@ hipError_t launch_split_merge(int out_dt, const float* part_out, const float* pa
 
 hipError_t launch_merge(int out_dt, const float* part_out, const float* part_lse,
                         const int32_t* seq_lens, int len_add, int window, int B, int H, int Dv,
-                        int T_max, int P, int NP, int xcd_group, void* out, hipStream_t stream) {
+                        int T_max, int P, int NP, void* out, hipStream_t stream) {
   if (out_dt == 0)
-    return launch_typed(part_out, part_lse, seq_lens, len_add, window, B, H, Dv, T_max, P, NP, xcd_group,
+    return launch_typed(part_out, part_lse, seq_lens, len_add, window, B, H, Dv, T_max, P, NP,
                         static_cast<float*>(out), stream);
-  return launch_typed(part_out, part_lse, seq_lens, len_add, window, B, H, Dv, T_max, P, NP, xcd_group,
+  return launch_typed(part_out, part_lse, seq_lens, len_add, window, B, H, Dv, T_max, P, NP,
                       static_cast<uint16_t*>(out), stream);
 }
 

@@ -49,7 +49,6 @@
 
 #include "device_util.h"
 #include "launch.h"
-#include "support.h"
 
 namespace attn {
 namespace {
@@ -475,10 +474,10 @@ void mla_partial_kernel(const MlaArgs a) {
   // The partial output goes out through LDS, one 32-dim slice at a time, so
   // that every store instruction writes whole 128-byte lines (8 heads x 32
   // dims) instead of 32-byte pieces of 32 rows. The stores use the default
-  // cache policy: the merge that follows reads each group's partials on the
-  // XCD that wrote them (the placement above), so part of them comes from
-  // that XCD's L2 (measured: 1.5-2 us less per call than non-temporal stores,
-  // same bits).
+  // cache policy: the merge that runs next reads them back faster than after
+  // non-temporal stores (measured 15.6 against 17.1 us per merge; the bytes
+  // it fetches past the L2 are the same, so the gain lies beyond the L2, most
+  // likely in the last-level cache).
   // The staging area is this wave's own blocks of the buffer after the last
   // tile's: no other wave reads that buffer any more, and this wave's copies
   // into it have landed. In block k, head 8k + c holds the eight 16-byte
@@ -515,7 +514,7 @@ void mla_partial_kernel(const MlaArgs a) {
 
 template <bool PAGED>
 hipError_t launch_mla_nhb(const MlaArgs& a, hipStream_t stream) {
-  const int nhb = mla_waves(a.H);
+  const int nhb = a.H >= 128 ? 4 : a.H / 32;  // 32-head blocks (waves) per work-group
   const long long groups = (long long)a.NP * (a.H / (32 * nhb)) * a.B;
   if (groups > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)groups);

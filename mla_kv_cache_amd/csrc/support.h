@@ -35,20 +35,6 @@ inline bool mla_supported(int H, int d_c, int d_r) {
   return d_c == 512 && d_r == 64 && H >= 32 && H % 32 == 0 && (H <= 128 || H % 128 == 0);
 }
 
-// Waves (32-head blocks) per work-group of the MLA partial kernel.
-inline int mla_waves(int H) { return H >= 128 ? 4 : H / 32; }
-
-// The MLA partial kernel hands the work-groups of each (sequence, head block)
-// group to one XCD (group g on XCD g % 8) when its grid of
-// NP * (H / (32 * waves)) * B work-groups is a multiple of 8 * NP; the merge
-// then reads each group's rows on the same XCD. Rows per group, or 0 when the
-// placement does not apply.
-inline int mla_xcd_group(int B, int H, int NP) {
-  const int nw = mla_waves(H);
-  const long long groups = (long long)NP * (H / (32 * nw)) * B;
-  return groups % (8LL * NP) == 0 ? 32 * nw : 0;
-}
-
 // MLA absorption products on 32x32x16 matrix-core tiles.
 inline bool absorb_supported(int d_h, int d_c) { return d_h >= 16 && d_h % 16 == 0 && d_c >= 32 && d_c % 32 == 0; }
 inline bool up_supported(int d_c, int d_v) { return d_c >= 16 && d_c % 16 == 0 && d_v >= 32 && d_v % 32 == 0; }

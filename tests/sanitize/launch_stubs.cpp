@@ -30,7 +30,7 @@ hipError_t launch_split_merge(int, const float*, const float*, const int32_t*, i
 hipError_t launch_kv_append(int, const void*, const void*, void*, void*, const int32_t*, int, int, int,
                             int, hipStream_t) { return reached(); }
 hipError_t launch_merge(int, const float*, const float*, const int32_t*, int, int, int, int, int, int,
-                        int, int, int, void*, hipStream_t) { return reached(); }
+                        int, int, void*, hipStream_t) { return reached(); }
 hipError_t launch_mla_partial(const MlaArgs&, hipStream_t) { return reached(); }
 hipError_t launch_latent_append(const void*, void*, const int32_t*, int, int, int, hipStream_t) {
   return reached();

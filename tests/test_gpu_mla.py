@@ -54,8 +54,8 @@ CASES = [
     (2, 128, 40, [5, 40]),
     (4, 128, 4096, [4096, 700, 0, 2049]),     # 16 partitions of 256: rows of 16, 3, 0 and 9 of them
     (1, 128, 65536, [65536]),                 # 256 partitions of one row, merged by the last
-    # sequence counts that are multiples of 8: the merge takes each group's rows on the
-    # XCD of its partials (groups of 128 rows; two head blocks per sequence for H = 256)
+    # sequence counts that are multiples of 8: the partial kernel places each (sequence,
+    # head block) on one XCD (two head blocks per sequence for H = 256)
     (8, 128, 1024, [1024, 1, 0, 777, 512, 1000, 33, 900]),
     (8, 256, 520, [520, 17, 300, 0, 519, 64, 2, 256]),
 ]
